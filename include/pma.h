@@ -1,0 +1,218 @@
+/*
+ * pma.h -- C ABI of libpma: packed masked attention and the MiniMax-H3 DiT
+ * block on AMD Instinct MI355X (gfx950).
+ *
+ * Every entry point takes plain pointers and sizes.  Unless stated otherwise
+ * a pointer argument is a DEVICE pointer owned by the caller; the library
+ * never allocates or frees device memory and keeps no state between calls
+ * beyond a per-thread error string and a per-device property cache.  Kernels
+ * are launched asynchronously on `stream` (a hipStream_t; NULL = the default
+ * stream); a call returns once its kernels are queued.  Calls on different
+ * streams are independent.  No C++ exception crosses this interface.
+ *
+ * Errors: argument checks that need no device data run on the host before any
+ * launch and return a status without launching anything.  Checks that depend
+ * on device data (the packed layout's contents) are done by a kernel that
+ * writes a status word into the layout workspace; pma_layout_read_status()
+ * reads it back.  HIP runtime failures return PMA_ERR_DEVICE.  On every
+ * non-OK return, pma_last_error() gives a human-readable detail string for
+ * the calling thread.
+ *
+ * Pages cited (by title and section):
+ *   [H3]  "MiniMaxH3Transformer3DModel" -- diffusers API page: intro,
+ *         constructor parameters, class description, forward parameters.
+ *   [ENG] "MiniMax H3 Inference Engine voor Mac computers" -- implementation
+ *         notes ("Exacte DiT fusions", "Metal 4 en TensorOps pads",
+ *         "Checkpoint layout en media pipeline", "Scheduling en
+ *         activatiegeheugen").
+ *
+ * Storage types: bf16 tensors are passed as pma_bf16 (the raw 16-bit
+ * pattern); every fp32 -> bf16 store rounds to nearest, ties to even.
+ */
+#ifndef PMA_H_
+#define PMA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t pma_bf16; /* bfloat16 bit pattern */
+
+typedef enum {
+    PMA_OK = 0,
+    PMA_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    PMA_ERR_SHAPE = 2,       /* a size, count or parameter is out of range     */
+    PMA_ERR_ALIGN = 3,       /* a pointer or leading dimension is misaligned   */
+    PMA_ERR_WORKSPACE = 4,   /* the workspace is smaller than required         */
+    PMA_ERR_LAYOUT = 5,      /* the packed layout failed validation            */
+    PMA_ERR_DEVICE = 6,      /* a HIP runtime call failed                      */
+    PMA_ERR_UNSUPPORTED = 7  /* device is not gfx950, or unsupported option    */
+} pma_status;
+
+/* Static name of a status code. */
+const char *pma_status_string(pma_status s);
+/* Detail of the calling thread's last failed call ("" if none). */
+const char *pma_last_error(void);
+/* PMA_OK if the current HIP device is a gfx950; PMA_ERR_UNSUPPORTED if not. */
+pma_status pma_device_check(void);
+
+/* ======================================================================
+ * 1. Packed layout -> documents and tile map
+ * ----------------------------------------------------------------------
+ * [H3] forward parameters: one packed 1-D sequence of L rows described by
+ * token_tags (0 video, 1 text, 2 audio), position_ids (t, h, w) per row,
+ * timestep_indices per row into T distinct timesteps, and three index
+ * tensors with the positions of the video, audio and text rows.  [H3] intro:
+ * rows tagged -1 are padding and form their own attention document through
+ * a boolean mask; [H3] class description: the original reference splits the
+ * padded tail off as its own varlen document.
+ *
+ * Document rule: row i may attend to row j iff (tag_i == -1) == (tag_j == -1).
+ * All padding rows are one document, all other rows the other one.
+ * ====================================================================== */
+
+/* Layout status bits (OR-ed into the status word by pma_layout_build). */
+#define PMA_LAYOUT_BAD_TAG        (1 << 0) /* tag not in {-1, 0, 1, 2}                 */
+#define PMA_LAYOUT_BAD_TIMESTEP   (1 << 1) /* non-padding row, index outside [0, T)    */
+#define PMA_LAYOUT_BAD_POSITION   (1 << 2) /* a position with |p| >= 2^24               */
+#define PMA_LAYOUT_BAD_INDEX      (1 << 3) /* index tensor entry outside [0, L)         */
+#define PMA_LAYOUT_UNSORTED_INDEX (1 << 4) /* index tensor not strictly ascending       */
+#define PMA_LAYOUT_INDEX_TAG      (1 << 5) /* index names a row of another modality     */
+#define PMA_LAYOUT_INDEX_COUNT    (1 << 6) /* count != number of rows with that tag     */
+
+/* Tile classes of the (tile_m x tile_n) tiling of the L x L mask, over the
+ * in-range pairs of each tile. */
+#define PMA_TILE_EMPTY   0 /* no allowed pair: never visited   */
+#define PMA_TILE_PARTIAL 1 /* some pairs allowed: masked tile  */
+#define PMA_TILE_FULL    2 /* every in-range pair allowed      */
+
+typedef struct {
+    int32_t seq_len;                  /* L >= 1                                      */
+    int32_t num_timesteps;            /* T >= 1                                      */
+    const int32_t *token_tags;        /* [L]                                         */
+    const int32_t *position_ids;      /* [L][3]  (t, h, w)                           */
+    const int32_t *timestep_indices;  /* [L]     ignored on padding rows             */
+    const int32_t *video_indices;     /* [num_video] ascending (NULL iff count 0)    */
+    const int32_t *audio_indices;     /* [num_audio]                                 */
+    const int32_t *text_indices;      /* [num_text]                                  */
+    int32_t num_video, num_audio, num_text;
+} pma_layout_desc;
+
+/* A built layout: plain data, device pointers into the caller's workspace
+ * plus copies of the descriptor's pointers.  Valid while the workspace and
+ * the descriptor's arrays are. */
+typedef struct {
+    int32_t seq_len, num_timesteps;
+    int32_t tile_m, tile_n;           /* tiling of the tile map                       */
+    int32_t num_q_tiles, num_k_tiles; /* ceil(L / tile_m), ceil(L / tile_n)           */
+    const int32_t *token_tags, *position_ids, *timestep_indices;
+    int32_t *doc;                     /* [L]  1 for padding rows, 0 otherwise          */
+    uint8_t *tile_class;              /* [num_q_tiles][num_k_tiles] PMA_TILE_*         */
+    int32_t *tile_count;              /* [num_q_tiles] non-EMPTY k-tiles per q-tile    */
+    int32_t *tile_list;               /* [num_q_tiles][num_k_tiles] ascending non-EMPTY
+                                         k-tiles, then -1                              */
+    int32_t *tile_order;              /* [num_q_tiles] q-tiles by (count desc, index asc) */
+    int32_t *status;                  /* [2] status bits, first row with a per-row error
+                                         (bad tag, timestep or position) or -1          */
+    int32_t *scratch;                 /* builder's internal counters                  */
+} pma_layout;
+
+/* Bytes of device workspace pma_layout_build needs. */
+pma_status pma_layout_workspace_size(int32_t seq_len, int32_t tile_m, int32_t tile_n,
+                                     size_t *bytes);
+
+/* Validate the layout and build document ids and the tile map.  tile_m and
+ * tile_n must each be 64, 128 or 256 (pass 0, 0 for the attention kernel's
+ * own tiling, see pma_attention_tiles).  workspace: >= the size above,
+ * 256-byte aligned.  Writes *out on the host; the device arrays are ready
+ * when the queued kernels finish.  The status word never makes a launch
+ * fail: read it with pma_layout_read_status. */
+pma_status pma_layout_build(const pma_layout_desc *desc, int32_t tile_m, int32_t tile_n,
+                            void *workspace, size_t workspace_bytes, void *stream,
+                            pma_layout *out);
+
+/* Synchronise `stream` and copy the status word to the host.  Returns
+ * PMA_ERR_LAYOUT if any status bit is set (PMA_OK otherwise); bits and
+ * first_bad_row may be NULL. */
+pma_status pma_layout_read_status(const pma_layout *layout, void *stream, int32_t *bits,
+                                  int32_t *first_bad_row);
+
+/* ======================================================================
+ * 2. Attention path: QK-RMSNorm + 3-axis RoPE, masked flash attention
+ * ----------------------------------------------------------------------
+ * [H3] constructor parameters: num_attention_heads (56), attention_head_dim
+ * (128), rope_freq_dim F (16): the t, h, w axes share one inv_freq buffer of
+ * length F and 2*3*F of the head's channels are rotated; rope_theta (1e4);
+ * qk_norm_eps (1e-5) of the per-head query/key norms.
+ *
+ * Computed, per row i and head h (readings of the pages' open points):
+ *   n = x * w / sqrt(mean(x^2) + qk_norm_eps)        RMSNorm over the head's D
+ *   axis a in {t,h,w}, f < F, phi = pos[i][a] * theta^(-f/F),
+ *   c0 = 2aF + f, c1 = c0 + F:
+ *     y[c0] = n[c0] cos phi - n[c1] sin phi,  y[c1] = n[c1] cos phi + n[c0] sin phi
+ *   y[c] = n[c] for c >= 6F.
+ *   O_i = sum_{j in doc(i)} softmax_j(scale * q'_i . k'_j) v_j,  scale = 1/sqrt(D)
+ * ====================================================================== */
+
+typedef struct {
+    int32_t num_heads;     /* H >= 1                                   */
+    int32_t head_dim;      /* D; must be 128                           */
+    int32_t rope_freq_dim; /* F; must be 8 or 16 (6F <= D)             */
+    float rope_theta;      /* > 0                                      */
+    float qk_norm_eps;     /* >= 0                                     */
+    float softmax_scale;   /* 0 selects 1/sqrt(D)                      */
+} pma_attn_params;
+
+/* The (tile_m, tile_n) the flash attention kernel needs its layout built with. */
+pma_status pma_attention_tiles(int32_t *tile_m, int32_t *tile_n);
+
+/* Padded row count Lp of the attention operands (L rounded up to 256). */
+pma_status pma_attention_padded_len(int32_t seq_len, int32_t *padded_len);
+
+/* QK-RMSNorm + 3-axis RoPE of Q and K, and relayout of Q, K, V into the
+ * attention kernel's operands.
+ *   q, k, v: token-major bf16, row i of head h at x[i*ld + h*D .. + D);
+ *            ld >= H*D, ld % 8 == 0, 16-byte aligned (the QKV projection
+ *            output [L][3*H*D] is used with ld = 3*H*D and offsets 0, HD, 2HD).
+ *   q_norm_weight, k_norm_weight: fp32 [D], shared by all heads.
+ *   qh, kh: bf16 [H][Lp][D] head-major normalised, rotated Q and K.
+ *   vt:     bf16 [H][D][Lp] V transposed per head (keys contiguous).
+ *   Rows L..Lp-1 of qh, kh and columns L..Lp-1 of vt are written as zero.
+ * [ENG] "Checkpoint layout en media pipeline" fuses the QK norm with RoPE;
+ * [ENG] "Metal 4 en TensorOps pads" feeds head-major attention inputs. */
+pma_status pma_qk_norm_rope(const pma_attn_params *p, const pma_layout *layout,
+                            const pma_bf16 *q, int64_t q_ld, const pma_bf16 *k,
+                            int64_t k_ld, const pma_bf16 *v, int64_t v_ld,
+                            const float *q_norm_weight, const float *k_norm_weight,
+                            pma_bf16 *qh, pma_bf16 *kh, pma_bf16 *vt, void *stream);
+
+/* Masked flash attention forward on the operands of pma_qk_norm_rope.
+ * layout must be built with pma_attention_tiles()' tiling.  Tiles the layout
+ * marks EMPTY are skipped whole; PARTIAL tiles and the ragged last k-tile
+ * apply the document/bounds mask.
+ *   o:   bf16 token-major, row i of head h at o[i*o_ld + h*D .. + D), o_ld >= H*D,
+ *        o_ld % 8 == 0.  Only rows < L are written.
+ *   lse: fp32 [H][L] natural-log sum of exp of the scaled logits (NULL: not written). */
+pma_status pma_flash_attention(const pma_attn_params *p, const pma_layout *layout,
+                               const pma_bf16 *qh, const pma_bf16 *kh, const pma_bf16 *vt,
+                               pma_bf16 *o, int64_t o_ld, float *lse, void *stream);
+
+/* Workspace of pma_attention: qh, kh and vt (3 * H * Lp * D bf16). */
+pma_status pma_attention_workspace_size(const pma_attn_params *p, int32_t seq_len,
+                                        size_t *bytes);
+
+/* pma_qk_norm_rope followed by pma_flash_attention; q, k, v are not modified. */
+pma_status pma_attention(const pma_attn_params *p, const pma_layout *layout,
+                         const pma_bf16 *q, int64_t q_ld, const pma_bf16 *k, int64_t k_ld,
+                         const pma_bf16 *v, int64_t v_ld, const float *q_norm_weight,
+                         const float *k_norm_weight, pma_bf16 *o, int64_t o_ld, float *lse,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PMA_H_ */

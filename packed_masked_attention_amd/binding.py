@@ -1,0 +1,239 @@
+"""ctypes binding of libpma (the C ABI in include/pma.h).
+
+Argument marshalling only: every function here forwards to the C entry point
+of the same name; all arithmetic runs in libpma's HIP kernels.  Device
+buffers are torch CUDA tensors (PyTorch provides memory and streams only) and
+are passed as raw pointers.  Loading fails loudly when libpma.so is missing:
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpma.so")
+
+PMA_OK = 0
+STATUS_NAMES = ["PMA_OK", "PMA_ERR_NULL", "PMA_ERR_SHAPE", "PMA_ERR_ALIGN", "PMA_ERR_WORKSPACE",
+                "PMA_ERR_LAYOUT", "PMA_ERR_DEVICE", "PMA_ERR_UNSUPPORTED"]
+TILE_EMPTY, TILE_PARTIAL, TILE_FULL = 0, 1, 2
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+
+class PmaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__(f"{name}: {detail}")
+
+
+class LayoutDesc(ctypes.Structure):
+    _fields_ = [("seq_len", _i32), ("num_timesteps", _i32),
+                ("token_tags", _vp), ("position_ids", _vp), ("timestep_indices", _vp),
+                ("video_indices", _vp), ("audio_indices", _vp), ("text_indices", _vp),
+                ("num_video", _i32), ("num_audio", _i32), ("num_text", _i32)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("seq_len", _i32), ("num_timesteps", _i32), ("tile_m", _i32), ("tile_n", _i32),
+                ("num_q_tiles", _i32), ("num_k_tiles", _i32),
+                ("token_tags", _vp), ("position_ids", _vp), ("timestep_indices", _vp),
+                ("doc", _vp), ("tile_class", _vp), ("tile_count", _vp), ("tile_list", _vp),
+                ("tile_order", _vp), ("status", _vp), ("scratch", _vp)]
+
+
+class AttnParams(ctypes.Structure):
+    _fields_ = [("num_heads", _i32), ("head_dim", _i32), ("rope_freq_dim", _i32),
+                ("rope_theta", ctypes.c_float), ("qk_norm_eps", ctypes.c_float),
+                ("softmax_scale", ctypes.c_float)]
+
+
+_SIGS = {
+    "pma_status_string": (ctypes.c_char_p, [_i32]),
+    "pma_last_error": (ctypes.c_char_p, []),
+    "pma_device_check": (_i32, []),
+    "pma_layout_workspace_size": (_i32, [_i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
+    "pma_layout_build": (_i32, [ctypes.POINTER(LayoutDesc), _i32, _i32, _vp, ctypes.c_size_t, _vp,
+                                ctypes.POINTER(Layout)]),
+    "pma_layout_read_status": (_i32, [ctypes.POINTER(Layout), _vp, ctypes.POINTER(_i32),
+                                      ctypes.POINTER(_i32)]),
+    "pma_attention_tiles": (_i32, [ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+    "pma_attention_padded_len": (_i32, [_i32, ctypes.POINTER(_i32)]),
+    "pma_qk_norm_rope": (_i32, [ctypes.POINTER(AttnParams), ctypes.POINTER(Layout), _vp, _i64, _vp,
+                                _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "pma_flash_attention": (_i32, [ctypes.POINTER(AttnParams), ctypes.POINTER(Layout), _vp, _vp,
+                                   _vp, _vp, _i64, _vp, _vp]),
+    "pma_attention_workspace_size": (_i32, [ctypes.POINTER(AttnParams), _i32,
+                                            ctypes.POINTER(ctypes.c_size_t)]),
+    "pma_attention": (_i32, [ctypes.POINTER(AttnParams), ctypes.POINTER(Layout), _vp, _i64, _vp,
+                             _i64, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, ctypes.c_size_t,
+                             _vp]),
+}
+
+_lib = None
+
+
+def lib():
+    """Load libpma.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m packed_masked_attention_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    return list(_SIGS)
+
+
+def check(status: int) -> None:
+    if status != PMA_OK:
+        raise PmaError(status, lib().pma_last_error().decode())
+
+
+def ptr(t) -> int | None:
+    """Device pointer of a torch tensor (None for None)."""
+    return None if t is None else t.data_ptr()
+
+
+def stream_ptr(stream=None) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+# ------------------------------------------------------------------ layout
+
+def pma_layout_workspace_size(seq_len: int, tile_m: int = 0, tile_n: int = 0) -> int:
+    n = ctypes.c_size_t()
+    check(lib().pma_layout_workspace_size(seq_len, tile_m, tile_n, ctypes.byref(n)))
+    return n.value
+
+
+class DeviceLayout:
+    """A built layout: the device arrays of the packed layout, the workspace
+    the builder wrote into, and the pma_layout struct."""
+
+    def __init__(self, arrays: dict, workspace, layout: Layout, desc: LayoutDesc):
+        self.arrays = arrays
+        self.workspace = workspace
+        self.struct = layout
+        self.desc = desc
+
+    @property
+    def seq_len(self) -> int:
+        return self.struct.seq_len
+
+
+def pma_layout_build(layout: dict, device="cuda", tile_m: int = 0, tile_n: int = 0,
+                     stream=None) -> DeviceLayout:
+    """Copy a host layout (see synth.layout_from_tags) to the device and build it."""
+    import torch
+    arr = {}
+    for k in ("tags", "pos", "ts_idx", "video_idx", "audio_idx", "text_idx"):
+        a = np.ascontiguousarray(np.asarray(layout[k], dtype=np.int32))
+        arr[k] = torch.from_numpy(a).to(device) if a.size else None
+    L = int(np.asarray(layout["tags"]).size)
+    desc = LayoutDesc(L, int(layout["T"]), ptr(arr["tags"]), ptr(arr["pos"]), ptr(arr["ts_idx"]),
+                      ptr(arr["video_idx"]), ptr(arr["audio_idx"]), ptr(arr["text_idx"]),
+                      int(np.asarray(layout["video_idx"]).size),
+                      int(np.asarray(layout["audio_idx"]).size),
+                      int(np.asarray(layout["text_idx"]).size))
+    nbytes = pma_layout_workspace_size(L, tile_m, tile_n)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    out = Layout()
+    check(lib().pma_layout_build(ctypes.byref(desc), tile_m, tile_n, ptr(ws), nbytes,
+                                 stream_ptr(stream), ctypes.byref(out)))
+    return DeviceLayout(arr, ws, out, desc)
+
+
+def pma_layout_read_status(dl: DeviceLayout, stream=None) -> tuple[int, int]:
+    """(status bits, first bad row); does not raise on a non-zero status."""
+    bits, row = _i32(), _i32()
+    st = lib().pma_layout_read_status(ctypes.byref(dl.struct), stream_ptr(stream),
+                                      ctypes.byref(bits), ctypes.byref(row))
+    if st not in (PMA_OK, 5):
+        check(st)
+    return bits.value, row.value
+
+
+def layout_arrays(dl: DeviceLayout) -> dict:
+    """Copy the built layout's device arrays to host numpy arrays."""
+    import torch
+    s = dl.struct
+    nqt, nkt, L = s.num_q_tiles, s.num_k_tiles, s.seq_len
+    ws = dl.workspace
+    base = ws.data_ptr()
+
+    def view(p, n, dtype):
+        off = p - base
+        esz = torch.tensor([], dtype=dtype).element_size()
+        return ws[off:off + n * esz].view(dtype).cpu().numpy()
+
+    return {"doc": view(s.doc, L, torch.int32),
+            "cls": view(s.tile_class, nqt * nkt, torch.uint8).reshape(nqt, nkt),
+            "count": view(s.tile_count, nqt, torch.int32),
+            "list": view(s.tile_list, nqt * nkt, torch.int32).reshape(nqt, nkt),
+            "order": view(s.tile_order, nqt, torch.int32)}
+
+
+# --------------------------------------------------------------- attention
+
+def attn_params(H: int, D: int = 128, F: int = 16, theta: float = 10000.0, eps: float = 1e-5,
+                scale: float = 0.0) -> AttnParams:
+    return AttnParams(H, D, F, theta, eps, scale)
+
+
+def pma_attention_tiles() -> tuple[int, int]:
+    m, n = _i32(), _i32()
+    check(lib().pma_attention_tiles(ctypes.byref(m), ctypes.byref(n)))
+    return m.value, n.value
+
+
+def pma_attention_padded_len(seq_len: int) -> int:
+    out = _i32()
+    check(lib().pma_attention_padded_len(seq_len, ctypes.byref(out)))
+    return out.value
+
+
+def pma_qk_norm_rope(p: AttnParams, dl: DeviceLayout, q, q_ld, k, k_ld, v, v_ld, wq, wk,
+                     qh, kh, vt, stream=None) -> None:
+    check(lib().pma_qk_norm_rope(ctypes.byref(p), ctypes.byref(dl.struct), ptr(q), q_ld, ptr(k),
+                                 k_ld, ptr(v), v_ld, ptr(wq), ptr(wk), ptr(qh), ptr(kh), ptr(vt),
+                                 stream_ptr(stream)))
+
+
+def pma_flash_attention(p: AttnParams, dl: DeviceLayout, qh, kh, vt, o, o_ld, lse=None,
+                        stream=None) -> None:
+    check(lib().pma_flash_attention(ctypes.byref(p), ctypes.byref(dl.struct), ptr(qh), ptr(kh),
+                                    ptr(vt), ptr(o), o_ld, ptr(lse), stream_ptr(stream)))
+
+
+def pma_attention_workspace_size(p: AttnParams, seq_len: int) -> int:
+    n = ctypes.c_size_t()
+    check(lib().pma_attention_workspace_size(ctypes.byref(p), seq_len, ctypes.byref(n)))
+    return n.value
+
+
+def pma_attention(p: AttnParams, dl: DeviceLayout, q, q_ld, k, k_ld, v, v_ld, wq, wk, o, o_ld,
+                  lse=None, workspace=None, stream=None) -> None:
+    import torch
+    nbytes = pma_attention_workspace_size(p, dl.seq_len)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    check(lib().pma_attention(ctypes.byref(p), ctypes.byref(dl.struct), ptr(q), q_ld, ptr(k),
+                              k_ld, ptr(v), v_ld, ptr(wq), ptr(wk), ptr(o), o_ld, ptr(lse),
+                              ptr(workspace), workspace.numel(), stream_ptr(stream)))

@@ -1,0 +1,76 @@
+// internal.h -- types and launchers shared by the libpma translation units.
+// gfx950 only: wave64, bf16 MFMA, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pma.h"
+
+namespace pma {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr int kHeadDim = 128;   // the only head size the kernels are built for
+constexpr int kPadRows = 256;   // attention operands are padded to a multiple of this
+
+// bf16 bits <-> fp32 (exact widening; RNE narrowing through the hardware convert)
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    bf16x2 r = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// ------------------------------------------------------------------ layout
+struct LayoutLaunch {
+    int32_t L, T, tile_m, tile_n, nqt, nkt;
+    const int32_t *tags, *pos, *ts_idx;
+    const int32_t *vid, *aud, *txt;
+    int32_t nv, na, nt;
+    int32_t *doc;
+    uint8_t *cls;
+    int32_t *count, *list, *order, *status;
+    int32_t *scratch;  // [0..2] tag counts, then q-tile flags [nqt], k-tile flags [nkt]
+};
+hipError_t launch_layout_build(const LayoutLaunch &a, hipStream_t s);
+
+// ------------------------------------------------------------- norm + rope
+struct PrepLaunch {
+    int32_t L, Lp, H, F;
+    float eps;
+    double inv_freq[16];
+    const uint16_t *q, *k, *v;
+    int64_t q_ld, k_ld, v_ld;
+    const float *wq, *wk;
+    const int32_t *pos;
+    uint16_t *qh, *kh, *vt;
+};
+hipError_t launch_qk_norm_rope(const PrepLaunch &a, hipStream_t s);
+
+// ----------------------------------------------------------------- flash
+struct FlashLaunch {
+    int32_t L, Lp, H, nqt, nkt;
+    float scale_log2;  // softmax_scale * log2(e)
+    float scale;       // softmax_scale
+    const uint16_t *qh, *kh, *vt;
+    uint16_t *o;
+    int64_t o_ld;
+    float *lse;
+    const int32_t *doc;
+    const uint8_t *cls;
+    const int32_t *count, *list, *order;
+};
+void flash_tiles(int32_t *tile_m, int32_t *tile_n);
+hipError_t launch_flash_attention(const FlashLaunch &a, hipStream_t s);
+
+}  // namespace pma

@@ -1,0 +1,167 @@
+// qk_norm_rope.hip -- per-head QK-RMSNorm + 3-axis RoPE, and the relayout of
+// Q, K, V into the flash attention kernel's operands.
+//
+// Page "MiniMaxH3Transformer3DModel" (diffusers API page), constructor
+// parameters: qk_norm_eps of the per-head query/key norms; rope_freq_dim F
+// frequencies per axis, one inv_freq buffer shared by the t, h and w axes,
+// 2*3*F rotated channels; rope_theta the base of the frequency schedule.
+// Page "MiniMax H3 Inference Engine voor Mac computers", checkpoint layout
+// notes: the QK normalisation and RoPE run as one fused kernel.
+//
+// Readings: RMSNorm over the head's 128 channels with one fp32 weight vector
+// shared by all heads; inv_freq[f] = theta^(-f/F); axis a rotates channel
+// pairs (2aF+f, 2aF+f+F) by pos[a]*inv_freq[f] (rotate-half pairing,
+// direction e^{+i phi}); channels >= 6F pass through.
+//
+// HBM-bound: per (row, head) it reads 3 x 256 B and writes 3 x 256 B.
+// Block = 64 rows x 4 heads.  Each 16-lane group owns one (row, head) of Q or
+// K, 8 channels (16 bytes) per lane; the sum of squares is reduced across the
+// group and the RoPE partner channels c +/- F sit F/8 lanes away.  cos/sin of
+// the 64 rows x 3F angles are computed once per block in fp64 (angles reach
+// ~1e3 rad, so no fast-math approximation) and kept in LDS as fp32.  V goes
+// through LDS and leaves transposed, keys contiguous per (head, channel).
+#include "internal.h"
+
+namespace pma {
+namespace {
+
+constexpr int kRows = 64;      // rows per block
+constexpr int kHeads = 4;      // heads per block
+constexpr int kThreads = 256;
+constexpr int kVRow = kHeadDim + 2;  // LDS row of the V tile in bf16: 65 words, so the
+                                     // transposed 2-byte reads spread over the banks
+
+__global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(PrepLaunch a) {
+    __shared__ float2 cs[kRows][48];                    // (cos, sin) per row, axis*F + f
+    __shared__ uint32_t vtile32[kRows * kVRow / 2];
+    uint16_t *vtile = reinterpret_cast<uint16_t *>(vtile32);
+
+    const int tid = threadIdx.x;
+    const int r0 = blockIdx.x * kRows;
+    const int h0 = blockIdx.y * kHeads;
+    const int nh = min(kHeads, a.H - h0);
+    const int F = a.F;
+    const int nang = 3 * F;
+
+    // ---- cos/sin table of this block's rows
+    for (int e = tid; e < kRows * nang; e += kThreads) {
+        const int rl = e / nang, j = e % nang;
+        const int row = r0 + rl;
+        float c = 1.f, s = 0.f;
+        if (row < a.L) {
+            const int ax = j / F, f = j % F;
+            const double phi = (double)a.pos[3 * (int64_t)row + ax] * a.inv_freq[f];
+            double sd, cd;
+            sincos(phi, &sd, &cd);
+            c = (float)cd;
+            s = (float)sd;
+        }
+        cs[rl][j] = make_float2(c, s);
+    }
+    __syncthreads();
+
+    // ---- Q and K: items (tensor, head, row) with rows fastest, 16 lanes each
+    const int chunk = tid & 15;          // channels 8*chunk .. 8*chunk+7
+    const int sub = tid >> 4;            // 16 items per pass
+    const int n_items = 2 * nh * kRows;
+    const int sec_chunks = F / 4;        // chunks per rotated section (2F channels)
+    const int half_chunks = F / 8;       // chunk distance of the partner channel
+    const bool rotated = chunk < 3 * sec_chunks;
+    const int ax = rotated ? chunk / sec_chunks : 0;
+    const int in_sec = chunk % sec_chunks;
+    const bool first_half = in_sec < half_chunks;
+    const int f0 = (first_half ? in_sec : in_sec - half_chunks) * 8;
+    for (int item = sub; item < n_items; item += kThreads / 16) {
+        const int rl = item % kRows;
+        const int hl = (item / kRows) % nh;
+        const int tensor = item / (kRows * nh);   // 0 = Q, 1 = K
+        const int row = r0 + rl;
+        const int h = h0 + hl;
+        const uint16_t *src = tensor ? a.k : a.q;
+        const int64_t ld = tensor ? a.k_ld : a.q_ld;
+        const float *w = tensor ? a.wk : a.wq;
+        uint16_t *dst = tensor ? a.kh : a.qh;
+
+        float x[8];
+        if (row < a.L) {
+            const u16x8 raw = *reinterpret_cast<const u16x8 *>(src + (int64_t)row * ld +
+                                                               h * kHeadDim + chunk * 8);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) x[t] = bf16_bits_to_f32(raw[t]);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) x[t] = 0.f;
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) ss = fmaf(x[t], x[t], ss);
+        ss += __shfl_xor(ss, 1, 16);
+        ss += __shfl_xor(ss, 2, 16);
+        ss += __shfl_xor(ss, 4, 16);
+        ss += __shfl_xor(ss, 8, 16);
+        const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
+        const f32x4 w0 = *reinterpret_cast<const f32x4 *>(w + chunk * 8);
+        const f32x4 w1 = *reinterpret_cast<const f32x4 *>(w + chunk * 8 + 4);
+        float n[8];
+        n[0] = x[0] * r * w0[0]; n[1] = x[1] * r * w0[1];
+        n[2] = x[2] * r * w0[2]; n[3] = x[3] * r * w0[3];
+        n[4] = x[4] * r * w1[0]; n[5] = x[5] * r * w1[1];
+        n[6] = x[6] * r * w1[2]; n[7] = x[7] * r * w1[3];
+        float y[8];
+        // partner channels: chunk +/- F/8 within the 16-lane group
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float pn = __shfl_xor(n[t], half_chunks, 16);
+            if (rotated) {
+                const float2 e = cs[rl][ax * F + f0 + t];
+                y[t] = first_half ? (n[t] * e.x - pn * e.y) : (n[t] * e.x + pn * e.y);
+            } else {
+                y[t] = n[t];
+            }
+        }
+        uint32_t packed[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) packed[t] = pack_bf16x2(y[2 * t], y[2 * t + 1]);
+        uint4 out = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        if (row >= a.L) out = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(dst + ((int64_t)h * a.Lp + row) * kHeadDim + chunk * 8) = out;
+    }
+
+    // ---- V: stage [64 rows][128] per head, write [128 channels][64 rows]
+    for (int hl = 0; hl < nh; ++hl) {
+        const int h = h0 + hl;
+        for (int e = tid; e < kRows * 16; e += kThreads) {
+            const int rl = e / 16, c8 = e % 16;
+            const int row = r0 + rl;
+            u16x8 raw = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (row < a.L)
+                raw = *reinterpret_cast<const u16x8 *>(a.v + (int64_t)row * a.v_ld +
+                                                       h * kHeadDim + c8 * 8);
+            const uint4 w4 = __builtin_bit_cast(uint4, raw);
+            uint32_t *d32 = vtile32 + (rl * kVRow + c8 * 8) / 2;
+            d32[0] = w4.x; d32[1] = w4.y; d32[2] = w4.z; d32[3] = w4.w;
+        }
+        __syncthreads();
+        // 128 channels x 8 row-groups of 8 rows; 8 consecutive lanes cover one
+        // channel's 64 rows (128 contiguous bytes)
+        for (int e = tid; e < kHeadDim * 8; e += kThreads) {
+            const int g = e % 8, c = e / 8;
+            u16x8 col;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) col[t] = vtile[(g * 8 + t) * kVRow + c];
+            *reinterpret_cast<u16x8 *>(a.vt + ((int64_t)h * kHeadDim + c) * a.Lp + r0 + g * 8) =
+                col;
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_qk_norm_rope(const PrepLaunch &a, hipStream_t s) {
+    dim3 grid(a.Lp / kRows, (a.H + kHeads - 1) / kHeads);
+    qk_norm_rope_kernel<<<grid, kThreads, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace pma

@@ -1,0 +1,71 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from packed_masked_attention_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "pma.h")) as fh:
+        text = fh.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(pma_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libpma.so not built")
+    return B.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) <= set(B.exported_symbols()) | set(names)
+    assert set(B.exported_symbols()) <= set(names)
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(B.STATUS_NAMES):
+        assert lib.pma_status_string(code).decode() == name
+
+
+def test_host_side_argument_errors(lib):
+    n = ctypes.c_size_t()
+    assert lib.pma_layout_workspace_size(0, 128, 64, ctypes.byref(n)) == 2
+    assert lib.pma_layout_workspace_size(100, 96, 64, ctypes.byref(n)) == 2
+    assert lib.pma_layout_workspace_size(100, 128, 64, None) == 1
+    assert lib.pma_layout_workspace_size(1000, 128, 64, ctypes.byref(n)) == 0 and n.value > 0
+    m, k = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.pma_attention_tiles(ctypes.byref(m), ctypes.byref(k)) == 0
+    assert (m.value, k.value) in {(128, 64), (256, 64)}
+    out = B.Layout()
+    assert lib.pma_layout_build(None, 0, 0, None, 0, None, ctypes.byref(out)) == 1
+    d = B.LayoutDesc(100, 1, None, None, None, None, None, None, 0, 0, 0)
+    assert lib.pma_layout_build(ctypes.byref(d), 0, 0, None, 0, None, ctypes.byref(out)) == 1
+    d = B.LayoutDesc(100, 0, 8, 8, 8, None, None, None, 0, 0, 0)
+    assert lib.pma_layout_build(ctypes.byref(d), 0, 0, 256, 1 << 20, None, ctypes.byref(out)) == 2
+    d = B.LayoutDesc(100, 1, 256, 256, 256, None, None, None, 0, 0, 0)
+    assert lib.pma_layout_build(ctypes.byref(d), 0, 0, 256, 16, None, ctypes.byref(out)) == 4
+    assert lib.pma_layout_build(ctypes.byref(d), 0, 0, 264, 1 << 20, None, ctypes.byref(out)) == 3
+    assert "aligned" in lib.pma_last_error().decode()
+    p = B.attn_params(4, D=64)
+    assert lib.pma_attention_workspace_size(ctypes.byref(p), 100, ctypes.byref(n)) == 7
+    p = B.attn_params(4, F=12)
+    assert lib.pma_attention_workspace_size(ctypes.byref(p), 100, ctypes.byref(n)) == 7
+    p = B.attn_params(56)
+    assert lib.pma_attention_workspace_size(ctypes.byref(p), 16384, ctypes.byref(n)) == 0
+    assert n.value == 3 * 56 * 16384 * 128 * 2
+    lp = ctypes.c_int32()
+    assert lib.pma_attention_padded_len(16385, ctypes.byref(lp)) == 0 and lp.value == 16640
+    lay = B.Layout()
+    assert lib.pma_flash_attention(ctypes.byref(p), ctypes.byref(lay), None, None, None, None, 0,
+                                   None, None) == 1

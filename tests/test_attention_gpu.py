@@ -1,0 +1,174 @@
+"""The attention path on the GPU (through the C ABI) vs the CPU oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from packed_masked_attention_amd import synth
+from tests.helpers import AttentionRun, assert_close, bf16_to_np, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _random_inputs(seed, L, H, pad_frac, scattered=True, scale=1.0):
+    rng = np.random.default_rng(seed)
+    lay = synth.random_layout(rng, L, pad_frac=pad_frac, scattered=scattered, max_pos=300)
+    q, k, v = (synth.normal_bf16(rng, (L, H, 128), scale) for _ in range(3))
+    return {"q": q, "k": k, "v": v, "layout": lay, "H": H, "D": 128}
+
+
+# ------------------------------------------------------------ norm + RoPE
+
+def _within_rounding(got, ref, name):
+    bound = np.abs(ref) * 2.0 ** -8 * (1 + 2.0 ** -6) + 2.0 ** -20
+    err = np.abs(got - ref)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{name}: {int(bad.sum())} values beyond one rounding; worst at {i}: "
+                             f"got {got[i]!r} ref {ref[i]!r}")
+
+
+@pytest.mark.parametrize("case", ["tiny", "random"])
+def test_qk_norm_rope_matches_oracle(case):
+    if case == "tiny":
+        inp = synth.make_attention_inputs(synth.workload("tiny_L256"))
+        w = None
+    else:
+        inp = _random_inputs(5, 777, 3, 0.1)
+        w = np.random.default_rng(6).uniform(0.5, 2.0, 128)
+    say(f"qk_norm_rope {case}")
+    r = AttentionRun(inp, wq=w, wk=w)
+    r.prep()
+    L, H = r.L, r.H
+    lay = inp["layout"]
+    wv = 1.0 if w is None else w.astype(np.float32).astype(np.float64)
+    for name, dev, src in (("Q", r.qh, inp["q"]), ("K", r.kh, inp["k"])):
+        got = bf16_to_np(dev)                       # [H, Lp, D]
+        ref = oracle.qk_norm_rope(src, H, 128, wv, lay["pos"])   # [L, H, D]
+        if w is None:   # unit weights: unit-variance outputs, the absolute bound applies
+            assert_close(got[:, :L].transpose(1, 0, 2), ref, f"{name}' (tol)")
+        # within one bf16 rounding (half an ulp, <= |x| 2^-8) of the fp64 value,
+        # plus fp32 slack for cancellation in the rotation
+        g = got[:, :L].transpose(1, 0, 2)
+        _within_rounding(g, ref, name)
+        # unrotated channels 96..127 are the rounded RMSNorm
+        nrm = oracle.qk_norm_rope(src, H, 128, wv, np.zeros((L, 3), np.int32))
+        _within_rounding(g[..., 96:], nrm[..., 96:], name + " passthrough")
+        assert np.all(got[:, L:] == 0)
+    vt = bf16_to_np(r.vt)                           # [H, D, Lp]
+    v = oracle.bf16_to_f64(inp["v"])                # [L, H, D]
+    assert np.array_equal(vt[:, :, :L], v.transpose(1, 2, 0))
+    assert np.all(vt[:, :, L:] == 0)
+
+
+# -------------------------------------------------------------- attention
+
+def _oracle_o(inp, rows=None, w=1.0, store_qk_bf16=False):
+    lay = inp["layout"]
+    return oracle.attention_path(inp["q"], inp["k"], inp["v"], lay, inp["H"], rows=rows, wq=w, wk=w,
+                                 store_qk_bf16=store_qk_bf16)
+
+
+@pytest.mark.parametrize("case", [
+    ("tiny_L256", None),
+    ("random_L1000_scattered", (11, 1000, 4, 0.2, True)),
+    ("random_L777_tail", (12, 777, 3, 0.1, False)),
+    ("random_L64_allpad", (13, 64, 2, 1.0, True)),
+    ("random_L1", (14, 1, 2, 0.0, True)),
+    ("random_L2500_nopad", (15, 2500, 2, 0.0, True)),
+])
+def test_attention_full_parity(case):
+    name, args = case
+    inp = synth.make_attention_inputs(synth.workload(name)) if args is None else _random_inputs(*args)
+    say(f"attention full parity {name}")
+    r = AttentionRun(inp).run()
+    ref, lse = _oracle_o(inp)
+    assert_close(r.out(), ref, name)
+    assert np.allclose(r.lse_np(), lse, atol=2e-2, rtol=0), "lse"
+
+
+@pytest.mark.parametrize("name", ["nopad_L4096", "masked_L16384", "long_L32768"])
+def test_attention_workload_sampled_rows(name):
+    wl = synth.workload(name)
+    inp = synth.make_attention_inputs(wl)
+    rows = sample_rows(inp["layout"], 160, seed=wl.seed)
+    if name == "long_L32768":
+        rows = rows[np.random.default_rng(0).permutation(rows.size)[:240]]
+        rows.sort()
+    say(f"attention sampled parity {name}: {rows.size} rows")
+    r = AttentionRun(inp).run()
+    got = r.out()[rows]
+    ref, lse = _oracle_o(inp, rows=rows)
+    st = assert_close(got, ref, name)
+    assert np.allclose(r.lse_np()[rows], lse, atol=2e-2, rtol=0)
+    say(f"  {name} sampled rows ok: {st}")
+
+
+def test_attention_sharpened_logits():
+    """QK-norm weights 4 scale the logits by 16 (std ~16), so the online max
+    changes often and the softmax is peaked.  At that scale one bf16 rounding
+    of the stored Q' and K' moves a logit by ~0.1, so the oracle stores Q' and
+    K' in bf16 exactly as the GPU path does.  Residual differences: where the
+    fp64 and the fp32 value of a Q'/K' element round to neighbouring bf16
+    values, a logit moves by up to 16 * 2^-8 * |k_c| ~ 0.06 and a peaked row
+    follows it; bf16 P adds 2^-9 relative per weight.  Bound: max 6e-2, mean
+    and relative as for unit logits."""
+    inp = _random_inputs(21, 1500, 2, 0.1)
+    w = np.full(128, 4.0)
+    say("attention sharpened logits (QK-norm weights 4)")
+    r = AttentionRun(inp, wq=w, wk=w).run()
+    ref, _ = _oracle_o(inp, w=4.0, store_qk_bf16=True)
+    assert_close(r.out(), ref, "sharpened", max_abs=6e-2)
+
+
+def test_attention_structural():
+    import torch
+    inp = _random_inputs(31, 900, 2, 0.15)
+    L, H = 900, 2
+    say("attention structural: V=1, determinism, document isolation")
+    ones = dict(inp)
+    ones["v"] = np.full_like(inp["v"], 0x3F80)      # bf16 1.0
+    r = AttentionRun(ones).run()
+    assert np.abs(r.out() - 1.0).max() <= 2 ** -7
+    r = AttentionRun(inp).run()
+    o1 = r.o.clone()
+    r.flash()
+    torch.cuda.synchronize()
+    assert torch.equal(r.o.view(torch.int16), o1.view(torch.int16)), "not deterministic"
+    # changing the padding rows' K/V leaves every real row bit-identical, and back
+    pad = inp["layout"]["tags"] == -1
+    for which in (pad, ~pad):
+        mod = dict(inp)
+        rng = np.random.default_rng(32)
+        k2, v2 = inp["k"].copy(), inp["v"].copy()
+        k2[which] = synth.normal_bf16(rng, k2[which].shape, 3.0)
+        v2[which] = synth.normal_bf16(rng, v2[which].shape, 3.0)
+        mod["k"], mod["v"] = k2, v2
+        r2 = AttentionRun(mod).run()
+        keep = ~which
+        assert np.array_equal(r2.out()[keep], bf16_to_np(o1).reshape(L, H, 128)[keep])
+
+
+def test_attention_timestep_indices_have_no_effect():
+    inp = _random_inputs(41, 600, 2, 0.1)
+    say("attention: timestep indices do not change O")
+    a = AttentionRun(inp).run().out()
+    lay = dict(inp["layout"])
+    lay["T"] = 5
+    lay["ts_idx"] = np.random.default_rng(42).integers(0, 5, 600).astype(np.int32)
+    lay["ts_idx"][lay["tags"] == -1] = 0
+    b = AttentionRun(dict(inp, layout=lay)).run().out()
+    assert np.array_equal(a, b)
+
+
+def test_attention_one_call_entry_point():
+    import torch
+    from packed_masked_attention_amd import binding as B
+    inp = _random_inputs(51, 700, 3, 0.1)
+    say("attention: pma_attention (prep + flash in one call)")
+    r = AttentionRun(inp).run()
+    o2 = torch.empty_like(r.o)
+    HD = r.H * 128
+    B.pma_attention(r.p, r.dl, r.q, HD, r.k, HD, r.v, HD, r.wq, r.wk, o2, HD)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.view(torch.int16), r.o.view(torch.int16))
