@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Packed masked attention on one MI355X: TFLOP/s and fraction of bf16 MFMA peak.
+
+A step is one pass of the attention hot path over the masked L=16384 packed
+sequence (512 text rows, 14400 video rows on a (9,40,40) grid, 656 audio
+rows, 816 padding rows in their own document; 56 heads x 128 channels, bf16
+Q/K/V ~ N(0,1), seeded): layout build -> QK-RMSNorm + 3-axis RoPE -> masked
+flash attention, all through the libpma C ABI with inputs resident in HBM.
+
+value = algorithmic FLOPs / step time, algorithmic FLOPs = 4*H*D*sum_d n_d^2
+(only the (query, key) pairs the document mask allows).  The roofline object
+is the flash attention kernel alone, timed with HIP events on the stream it is
+launched on; the cpu_baseline object is the CPU oracle's fp32 attention loop
+timed on a bounded sample of query rows on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline] [--copy-probe BYTES]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6          # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+HBM_PEAK_GBS = 8000.0
+METRIC = "packed masked attention TFLOP/s + % bf16 MFMA peak at L=16384,H=56,D=128"
+COUNTERS = os.path.join(ROOT, "profiles", "flash_fwd_masked_L16384_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def attention_flops(tags, H: int, D: int) -> int:
+    import numpy as np
+    tags = np.asarray(tags)
+    npad = int((tags == -1).sum())
+    nreal = tags.size - npad
+    return 4 * H * D * (npad * npad + nreal * nreal)
+
+
+def traffic_from_profiles():
+    """HBM bytes per flash launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    if not os.path.exists(COUNTERS):
+        return None
+    with open(COUNTERS) as fh:
+        c = json.load(fh)
+    src = os.path.join(ROOT, "packed_masked_attention_amd", "csrc", "flash_fwd.hip")
+    if c.get("flash_fwd_sha256_16") != source_hash(src):
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp: dict, target_s: float = 12.0) -> dict:
+    """The oracle's fp32 two-pass attention on a random sample of query rows
+    (all heads), sized to roughly target_s seconds of CPU work."""
+    import numpy as np
+    import oracle
+    lay, H, D = inp["layout"], inp["H"], inp["D"]
+    L = lay["L"]
+    t0 = time.perf_counter()
+    qn = oracle.qk_norm_rope(inp["q"], H, D, 1.0, lay["pos"]).astype(np.float32)
+    kn = oracle.qk_norm_rope(inp["k"], H, D, 1.0, lay["pos"]).astype(np.float32)
+    v = oracle.bf16_to_f64(inp["v"]).astype(np.float32)
+    t_prep = time.perf_counter() - t0
+    tags = lay["tags"]
+    pad = tags == -1
+    n_doc = np.where(pad, pad.sum(), (~pad).sum())
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(L, size=16, replace=False)).astype(np.int32)
+    t0 = time.perf_counter()
+    oracle.attention(qn, kn, v, tags, rows=rows, precision="f32")
+    t_probe = time.perf_counter() - t0
+    n = int(min(L, max(16, 16 * target_s / max(t_probe, 1e-3))))
+    rows = np.sort(rng.choice(L, size=n, replace=False)).astype(np.int32)
+    t0 = time.perf_counter()
+    oracle.attention(qn, kn, v, tags, rows=rows, precision="f32")
+    t_attn = time.perf_counter() - t0
+    flops = 4 * H * D * int(n_doc[rows].sum())
+    return {"value": flops / t_attn / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"fp32 two-pass attention for {n} random query rows x {H} heads of "
+                      f"the L={L} workload ({t_attn:.1f} s); QK-norm+RoPE of all rows "
+                      f"took {t_prep:.1f} s and is not in the rate"}
+
+
+def copy_probe(nbytes: int) -> None:
+    """A plain device copy of known size, for scaling rocprofv3 HBM counters."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="masked_L16384")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe", type=int, default=0, help=argparse.SUPPRESS)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}); the path is built and measured on a single MI355X.", file=sys.stderr)
+        return 2
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return 0
+
+    import numpy as np
+    import torch
+    from packed_masked_attention_amd import binding as B
+    from packed_masked_attention_amd import synth
+
+    torch.cuda.set_device(0)
+    wl = synth.workload(args.workload)
+    log(f"[bench] generating {wl.name} inputs")
+    inp = synth.make_attention_inputs(wl)
+    lay = inp["layout"]
+    L, H, D = wl.L, wl.H, wl.D
+    flops = attention_flops(lay["tags"], H, D)
+
+    dev = torch.device("cuda", 0)
+    to_dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev) \
+        .view(torch.bfloat16)
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    wq = torch.ones(D, dtype=torch.float32, device=dev)
+    wk = torch.ones(D, dtype=torch.float32, device=dev)
+    dl = B.pma_layout_build(lay, device=dev)
+    bits, row = B.pma_layout_read_status(dl)
+    if bits:
+        raise RuntimeError(f"layout status {bits:#x} row {row}")
+    p = B.attn_params(H)
+    Lp = B.pma_attention_padded_len(L)
+    qh = torch.empty(H, Lp, D, dtype=torch.bfloat16, device=dev)
+    kh = torch.empty_like(qh)
+    vt = torch.empty(H, D, Lp, dtype=torch.bfloat16, device=dev)
+    o = torch.empty(L, H * D, dtype=torch.bfloat16, device=dev)
+    HD = H * D
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        B.pma_layout_build(dl)
+        B.pma_qk_norm_rope(p, dl, q, HD, k, HD, v, HD, wq, wk, qh, kh, vt)
+        if ev is not None:
+            ev[0].record(stream)
+        B.pma_flash_attention(p, dl, qh, kh, vt, o, HD)
+        if ev is not None:
+            ev[1].record(stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    flash_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (flash_ms * 1e-3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(inp, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "seq_len": L, "heads": H, "head_dim": D,
+                   "rows": {"text": wl.text, "video": wl.n_video, "audio": wl.audio,
+                            "padding": wl.pad},
+                   "video_grid": list(wl.video), "documents": sorted(
+                       {int((lay["tags"] == -1).sum()), int((lay["tags"] != -1).sum())} - {0},
+                       reverse=True),
+                   "algorithmic_flops": flops,
+                   "step": "layout build + QK-RMSNorm/RoPE + masked flash attention",
+                   "pct_bf16_peak_step": round(100 * value / BF16_PEAK_TFLOPS, 2)},
+        "roofline": {"kernel": "flash_fwd_kernel", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic_from_profiles(), "avg_ms": round(flash_ms, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -138,10 +138,20 @@ class DeviceLayout:
         return self.struct.seq_len
 
 
-def pma_layout_build(layout: dict, device="cuda", tile_m: int = 0, tile_n: int = 0,
+def pma_layout_build(layout, device="cuda", tile_m: int = 0, tile_n: int = 0,
                      stream=None) -> DeviceLayout:
-    """Copy a host layout (see synth.layout_from_tags) to the device and build it."""
+    """Build a layout.  ``layout`` is either a host layout dict (see
+    synth.layout_from_tags), copied to the device first, or a DeviceLayout,
+    rebuilt in place from its device-resident arrays and workspace."""
     import torch
+    if isinstance(layout, DeviceLayout):
+        dl = layout
+        out = Layout()
+        check(lib().pma_layout_build(ctypes.byref(dl.desc), dl.struct.tile_m, dl.struct.tile_n,
+                                     ptr(dl.workspace), dl.workspace.numel(), stream_ptr(stream),
+                                     ctypes.byref(out)))
+        dl.struct = out
+        return dl
     arr = {}
     for k in ("tags", "pos", "ts_idx", "video_idx", "audio_idx", "text_idx"):
         a = np.ascontiguousarray(np.asarray(layout[k], dtype=np.int32))
