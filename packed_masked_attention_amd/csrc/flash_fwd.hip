@@ -17,16 +17,23 @@
 //    converted to bf16, are the B operand P^T of O^T = V^T P^T with no data
 //    movement, and V^T (pre-transposed by the prep kernel, keys contiguous)
 //    is read from LDS in natural key order as the A operand.
-//  * Online softmax in fp32 with exp2 (log2 e folded into the scale), row sum
-//    by v_dot2 on the bf16 probabilities actually fed to the PV product, and
-//    the O rescale skipped when no row max grew.
+//  * Online softmax in fp32 with exp2 (log2 e folded into the scale) and a
+//    lazy reference max: a row's reference only moves when its max grows by
+//    more than 2^8 (so p <= 256, exact in fp32/bf16 range), which makes the
+//    O rescale rare.  Row sums by v_dot2 on the bf16 probabilities actually
+//    fed to the PV product.
+//  * Software pipelined: iteration j issues S(j+1) = K(j+1) Q^T in the same
+//    basic block as the softmax of S(j), so the MFMAs of one overlap the VALU
+//    of the other inside a wave; then O += V(j)^T P(j).  The K and V buffers
+//    run one tile apart (K(j+1) and V(j) are resident during iteration j).
 //  * Tiles come from the layout's per-q-tile list of non-EMPTY k-tiles: EMPTY
 //    tiles are never visited; FULL tiles take no mask ops; PARTIAL tiles and
 //    the ragged last k-tile mask by document bit / bounds from two ballots.
 //  * K and V^T tiles are double-buffered in LDS and filled by direct-to-LDS
-//    loads (global_load_lds_dwordx4): the next listed tile streams into the
-//    idle buffer while the current one is consumed, with no staging
-//    registers; one wait + barrier per tile.  Each wave-instruction fills
+//    buffer loads (buffer_load_dwordx4 ... lds) with the tile offset in an
+//    SGPR: the next tiles stream into the idle buffers while the current ones
+//    are consumed, with no staging registers and no per-tile address VALU;
+//    one wait + barrier per tile.  Each wave-instruction fills
 //    1 KB of LDS in lane order, so instead of row padding the 16-byte chunks
 //    of a row are XOR-swizzled (chosen by the global address each lane
 //    fetches), which keeps the MFMA-operand reads bank-conflict-free.
@@ -53,11 +60,19 @@ __device__ __forceinline__ int v_pos(int row, int c) { return c ^ ((row >> 1) & 
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// 16 bytes per lane from global memory straight into LDS (lane l lands at
-// lds + 16*l).  Kept out of the kernel template: with the builtin written in
-// the template body the host compilation pass drops the kernel's stub.
-__device__ __forceinline__ void dma16(const void *g, lds_void *l) {
-    __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+// Buffer resource word 3 for raw (untyped) dword loads.
+constexpr int kRsrcFlags = 0x00020000;
+
+// 16 bytes per lane from a buffer straight into LDS: lane l reads
+// base + voff + soff and lands at lds + 16*l.  Kept out of the kernel
+// template: with the builtin written in the template body the host
+// compilation pass drops the kernel's stub.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_void *l, uint32_t voff,
+                                      uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcFlags);
 }
 
 // Row of the 32-key K slab that lane i supplies as MFMA A-operand row i.
@@ -82,11 +97,12 @@ __device__ __forceinline__ float half_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int NW, int QB>
+template <int NW>
 __global__ __launch_bounds__(NW * 64, 2) void flash_fwd_kernel(FlashLaunch a) {
-    constexpr int BM = NW * 32 * QB;
-    constexpr int KI = 16 / NW;   // 1 KB direct-to-LDS instructions per wave for K (and for V^T)
+    constexpr int BM = NW * 32;
+    constexpr int KI = 16 / NW;   // 1 KB LDS-DMA instructions per wave per tile (K or V^T)
     static_assert(KI * NW == 16, "16 KB tiles split over the waves");
+    constexpr int kMask = 0x3fffffff;
 
     // two buffers per operand as four distinct objects, so the compiler can
     // tell the buffer being streamed into from the one being read
@@ -110,225 +126,235 @@ __global__ __launch_bounds__(NW * 64, 2) void flash_fwd_kernel(FlashLaunch a) {
     const int head = item / a.nqt;
     const int qt = a.order[item % a.nqt];
     const int cnt = a.count[qt];
-    const int32_t *list = a.list + (int64_t)qt * a.nkt;
-    const uint8_t *cls = a.cls + (int64_t)qt * a.nkt;
-    const uint16_t *kbase = a.kh + (int64_t)head * a.Lp * kD;
-    const uint16_t *vbase = a.vt + (int64_t)head * kD * a.Lp;
+    {
+        const int32_t *list = a.list + (int64_t)qt * a.nkt;
+        const uint8_t *cls = a.cls + (int64_t)qt * a.nkt;
+        for (int i = tid; i < cnt; i += NW * 64) {
+            const int kt = list[i];
+            const bool m = cls[kt] != PMA_TILE_FULL || (kt + 1) * kBN > a.L;
+            tlist[i] = kt | (m ? (1 << 30) : 0);
+        }
+    }
+    __syncthreads();   // the list is read by every wave from here on
+    const __amdgpu_buffer_rsrc_t krs =
+        make_rsrc(a.kh + (int64_t)head * a.Lp * kD, (uint32_t)a.Lp * kD * 2u);
+    const __amdgpu_buffer_rsrc_t vrs =
+        make_rsrc(a.vt + (int64_t)head * kD * a.Lp, (uint32_t)a.Lp * kD * 2u);
 
     // ---- Q^T fragments: lane holds query row l32, channels 16c + 8*hi + [0, 8)
-    const int q0 = qt * BM + wave * 32 * QB;
-    bf16x8 qf[QB][8];
+    const int q0 = qt * BM + wave * 32;
+    bf16x8 qf[8];
+    {
+        const uint16_t *qrow = a.qh + ((int64_t)head * a.Lp + q0 + l32) * kD + 8 * hi;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const uint16_t *qrow = a.qh + ((int64_t)head * a.Lp + q0 + qb * 32 + l32) * kD + 8 * hi;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) qf[qb][c] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * c);
+        for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * c);
     }
 
-    // ---- direct-to-LDS tile loads.  Wave-instruction j of the K tile fills
-    // rows 4j..4j+3 (lane l: row 4j + l/16, position l%16); of the V^T tile,
-    // rows 8j..8j+7 (lane l: row 8j + l/8, position l%8).  Each lane fetches
-    // the chunk the swizzle places at its position.
-    // byte offsets, 32-bit, so each load is SGPR base + VGPR offset
-    uint32_t kg[KI], vg[KI];
+    // ---- LDS-DMA lane offsets.  Wave-instruction j of the K tile fills rows
+    // 4j..4j+3 (lane l: row 4j + l/16, position l%16); of the V^T tile, rows
+    // 8j..8j+7 (lane l: row 8j + l/8, position l%8).  Each lane fetches the
+    // chunk the swizzle places at its position; the tile's own offset
+    // (kt * 64 keys) is the SGPR offset.
+    uint32_t kvo[KI], vvo[KI];
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
         const int j = wave * KI + i;
         const int kr = 4 * j + (lane >> 4), kp = lane & 15;
-        kg[i] = 2u * (uint32_t)(kr * kD + 8 * k_pos(kr, kp));
+        kvo[i] = 2u * (uint32_t)(kr * kD + 8 * k_pos(kr, kp));
         const int vr = 8 * j + (lane >> 3), vp = lane & 7;
-        vg[i] = 2u * ((uint32_t)vr * (uint32_t)a.Lp + 8u * v_pos(vr, vp));
+        vvo[i] = 2u * ((uint32_t)vr * (uint32_t)a.Lp + 8u * v_pos(vr, vp));
     }
-#define PMA_DMA_TILE(kt_, kdst_, vdst_)                                                      \
-    do {                                                                                     \
-        const char *kgb_ = reinterpret_cast<const char *>(kbase + (int64_t)(kt_) * kBN * kD); \
-        const char *vgb_ = reinterpret_cast<const char *>(vbase + (int64_t)(kt_) * kBN);    \
-        _Pragma("unroll") for (int i = 0; i < KI; ++i) {                                     \
-            const int j = wave * KI + i;                                                     \
-            dma16(kgb_ + kg[i], (lds_void *)&(kdst_)[j * 512]);                              \
-            dma16(vgb_ + vg[i], (lds_void *)&(vdst_)[j * 512]);                              \
-        }                                                                                    \
-    } while (0)
+    auto dma_k = [&](int kt, uint16_t *dst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < KI; ++i)
+            dma16(krs, (lds_void *)&dst[(wave * KI + i) * 512], kvo[i], (uint32_t)kt * (kBN * kD * 2));
+    };
+    auto dma_v = [&](int kt, uint16_t *dst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < KI; ++i)
+            dma16(vrs, (lds_void *)&dst[(wave * KI + i) * 512], vvo[i], (uint32_t)kt * (kBN * 2));
+    };
 
-    // ---- per-row state
-    float m[QB], lsum[QB];
-    int dq[QB];
-    f32x16 o[QB][4];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        m[qb] = -INFINITY;
-        lsum[qb] = 0.f;
-        const int qrow = q0 + qb * 32 + l32;
-        dq[qb] = qrow < a.L ? a.doc[qrow] : 0;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) o[qb][db][v] = 0.f;
-    }
-    const float c2 = a.scale_log2;
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    // ---- S^T = K Q^T over one K tile: two 32-key slabs
     const int krow = k_slab_row(l32);
-
-    for (int i = tid; i < cnt; i += NW * 64) {
-        const int kt = list[i];
-        const bool m = cls[kt] != PMA_TILE_FULL || (kt + 1) * kBN > a.L;
-        tlist[i] = kt | (m ? (1 << 30) : 0);
-    }
-    PMA_DMA_TILE(list[0], ks0, vs0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    auto step = [&](int it, const uint16_t *ksr, const uint16_t *vsr, uint16_t *ksw,
-                    uint16_t *vsw) __attribute__((always_inline)) {
-        const int entry = tlist[it];
-        const int kt = entry & 0x3fffffff;
-        // stream the next listed tile into the idle buffers
-        if (it + 1 < cnt) PMA_DMA_TILE(tlist[it + 1] & 0x3fffffff, ksw, vsw);
-
-        // ---- S^T = K Q^T for two 32-key slabs
-        f32x16 s[QB][2];
+    auto qk = [&](const uint16_t *kbuf, f32x16 (&s)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) s[qb][kb][v] = 0.f;
+            for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
             const int r = 32 * kb + krow;
-            const uint16_t *kp = ksr + r * kD;
+            const uint16_t *kp = kbuf + r * kD;
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kp + 8 * k_pos(r, 2 * c + hi));
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][c], s[qb][kb],
-                                                                        0, 0, 0);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
             }
+        }
+    };
+
+    // ---- document / bounds mask of a PARTIAL or ragged tile
+    const int qrow = q0 + l32;
+    const int dq = (uint32_t)qrow < (uint32_t)a.L ? a.doc[qrow] : 0;
+    auto apply_mask = [&](int kt, f32x16 (&s)[2]) __attribute__((always_inline)) {
+        const int key = kt * kBN + lane;
+        const int dk = (uint32_t)key < (uint32_t)a.L ? a.doc[key] : -1;
+        const uint64_t padm = __ballot(dk == 1), realm = __ballot(dk == 0);
+        const uint64_t allow = dq ? padm : realm;
+        // the lane's 32 keys are the bytes 16g + 8*hi (g = 0..3) of the tile;
+        // gather them so bit 16*kb + v is register (kb, v)
+        const uint32_t lo = (uint32_t)allow, hw = (uint32_t)(allow >> 32);
+        const uint32_t sh = 8u * hi;
+        const uint32_t m32 = ((lo >> sh) & 0xffu) | (((lo >> (16 + sh)) & 0xffu) << 8) |
+                             (((hw >> sh) & 0xffu) << 16) | (((hw >> (16 + sh)) & 0xffu) << 24);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                if (!((m32 >> (16 * kb + v)) & 1u)) s[kb][v] = -INFINITY;
+    };
+
+    // ---- per-row state: lazy reference max (log2 units), partial row sum, O^T
+    float mref = -INFINITY, lsum = 0.f;
+    f32x16 o[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
+    const float c2 = a.scale_log2;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+    // ---- prologue: K(0), V(0), K(1) resident; S(0) computed and masked
+    f32x16 s[2];
+    {
+        const int e0 = tlist[0];
+        dma_k(e0 & kMask, ks0);
+        dma_v(e0 & kMask, vs0);
+        if (cnt > 1) dma_k(tlist[1] & kMask, ks1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        qk(ks0, s);
+        if (e0 >> 30) apply_mask(e0 & kMask, s);
+        __syncthreads();   // every wave is done with ks0 before it is refilled
+    }
+
+    // iteration j: reads K(j+1) from kr and V(j) from vr; streams K(j+2) into
+    // kw and V(j+1) into vw
+    auto step = [&](int j, const uint16_t *kr, uint16_t *kw, const uint16_t *vr, uint16_t *vw)
+                    __attribute__((always_inline)) {
+        const bool has1 = j + 1 < cnt;
+        const int e1 = has1 ? tlist[j + 1] : 0;
+        if (j + 2 < cnt) dma_k(tlist[j + 2] & kMask, kw);
+        if (has1) dma_v(e1 & kMask, vw);
+
+        // S(j+1): issued unconditionally (a stale buffer past the end is read
+        // and discarded) so it shares a basic block with the softmax below
+        f32x16 sn[2];
+        qk(kr, sn);
+
+        // softmax of S(j) -> P(j)^T in bf16
+        float mx = s[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+        mx = half_max(mx) * c2;
+        const bool need = mx > mref + 8.0f;
+        const float mnew = need ? mx : mref;
+        const float alpha = need ? __builtin_amdgcn_exp2f(mref - mnew) : 1.0f;
+        mref = mnew;
+        const float mu = (mnew == -INFINITY) ? 0.f : mnew;
+        float rs = 0.f;
+        bf16x8 pf[4];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            bf16x2 pp[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[cc >> 1][8 * (cc & 1) + 2 * t], c2, -mu));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[cc >> 1][8 * (cc & 1) + 2 * t + 1], c2, -mu));
+                const f32x2 pv = {p0, p1};
+                pp[t] = __builtin_convertvector(pv, bf16x2);
+                rs = __builtin_amdgcn_fdot2_f32_bf16(pp[t], ones, rs, false);
+            }
+            pf[cc] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+                                             __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
+                                             0, 1, 2, 3, 4, 5, 6, 7);
+        }
+        lsum = fmaf(lsum, alpha, rs);
+        // interleave S(j+1)'s MFMAs with the softmax VALU: K fragment reads run
+        // two ahead, then 16 x {1 MFMA, 1 LDS read, 6 VALU}
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        }
+        // the row sum in the condition (never negative) keeps the softmax
+        // above this branch, in the block it shares with S(j+1)'s MFMAs
+        if (__ballot(need || !(rs >= 0.f))) {
+#pragma unroll
+            for (int db = 0; db < 4; ++db) o[db] *= alpha;
         }
 
-        // ---- mask (PARTIAL tiles and the ragged tail only)
-        if (entry >> 30) {
-            const int key = kt * kBN + lane;
-            const int dk = key < a.L ? a.doc[key] : -1;
-            const uint64_t padm = __ballot(dk == 1), realm = __ballot(dk == 0);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const uint64_t allow = dq[qb] ? padm : realm;
-                // the lane's 32 keys are the bytes 16g + 8*hi (g = 0..3) of the
-                // tile; gather them so bit 16*kb + v is register (kb, v)
-                const uint32_t lo = (uint32_t)allow, hi32 = (uint32_t)(allow >> 32);
-                const uint32_t sh = 8u * hi;
-                const uint32_t m32 = ((lo >> sh) & 0xffu) | (((lo >> (16 + sh)) & 0xffu) << 8) |
-                                     (((hi32 >> sh) & 0xffu) << 16) |
-                                     (((hi32 >> (16 + sh)) & 0xffu) << 24);
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        if (!((m32 >> (16 * kb + v)) & 1u)) s[qb][kb][v] = -INFINITY;
-            }
-        }
-        // ---- online softmax; P^T in bf16 straight from the accumulator registers
-        bf16x8 pf[QB][4];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            float mx = s[qb][0][0];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[qb][kb][v]);
-            mx = half_max(mx);
-            const float m_new = fmaxf(m[qb], mx);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f((m[qb] - m_use) * c2);
-            const bool grow = m_new > m[qb];
-            m[qb] = m_new;
-            const float mc = m_use * c2;
-            float rs = 0.f;
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                bf16x2 pp[4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][cc >> 1][8 * (cc & 1) + 2 * t], c2, -mc));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][cc >> 1][8 * (cc & 1) + 2 * t + 1], c2, -mc));
-                    const f32x2 pv = {p0, p1};
-                    pp[t] = __builtin_convertvector(pv, bf16x2);
-                    rs = __builtin_amdgcn_fdot2_f32_bf16(pp[t], ones, rs, false);
-                }
-                pf[qb][cc] = __builtin_shufflevector(
-                    __builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
-                    __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-            }
-            lsum[qb] = fmaf(lsum[qb], alpha, rs);
-            if (__ballot(grow)) {
-#pragma unroll
-                for (int db = 0; db < 4; ++db) o[qb][db] *= alpha;
-            }
-        }
-
-        // ---- O^T += V^T P^T
+        // O^T += V(j)^T P(j)^T
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
             const int d = 32 * db + l32;
-            const uint16_t *vp = vsr + d * kBN;
+            const uint16_t *vp = vr + d * kBN;
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
                 const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(vp + 8 * v_pos(d, 2 * cc + hi));
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][cc], o[qb][db],
-                                                                        0, 0, 0);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[cc], o[db], 0, 0, 0);
             }
         }
 
-        __builtin_amdgcn_s_waitcnt(0);   // the streamed tile has landed
+        if (has1 && (e1 >> 30)) apply_mask(e1 & kMask, sn);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = sn[kb];
+        __builtin_amdgcn_s_waitcnt(0);   // the streamed tiles have landed
         __syncthreads();
     };
 
-    for (int it = 0; it < cnt; it += 2) {
-        step(it, ks0, vs0, ks1, vs1);
-        if (it + 1 < cnt) step(it + 1, ks1, vs1, ks0, vs0);
+    for (int j = 0; j < cnt; j += 2) {
+        step(j, ks1, ks0, vs0, vs1);
+        if (j + 1 < cnt) step(j + 1, ks0, ks1, vs1, vs0);
     }
 
     // ---- epilogue: O row = O^T column / row sum; register v of d-block db is
     // channel 32*db + 8*(v/4) + 4*hi + v%4
+    const float lt = half_sum(lsum);
+    const float inv = 1.0f / lt;
+    if (qrow < a.L) {
+        uint16_t *orow = a.o + (int64_t)qrow * a.o_ld + head * kD + 4 * hi;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float lt = half_sum(lsum[qb]);
-        const float inv = 1.0f / lt;
-        const int qrow = q0 + qb * 32 + l32;
-        if (qrow < a.L) {
-            uint16_t *orow = a.o + (int64_t)qrow * a.o_ld + head * kD + 4 * hi;
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    uint2 w;
-                    w.x = pack_bf16x2(o[qb][db][4 * g] * inv, o[qb][db][4 * g + 1] * inv);
-                    w.y = pack_bf16x2(o[qb][db][4 * g + 2] * inv, o[qb][db][4 * g + 3] * inv);
-                    *reinterpret_cast<uint2 *>(orow + 32 * db + 8 * g) = w;
-                }
-            if (a.lse && hi == 0) a.lse[(int64_t)head * a.L + qrow] = m[qb] * a.scale + logf(lt);
-        }
+            for (int g = 0; g < 4; ++g) {
+                uint2 w;
+                w.x = pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+                w.y = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+                *reinterpret_cast<uint2 *>(orow + 32 * db + 8 * g) = w;
+            }
+        if (a.lse && hi == 0)
+            a.lse[(int64_t)head * a.L + qrow] = (mref + __log2f(lt)) * 0.69314718055994531f;
     }
 }
 
-#undef PMA_DMA_TILE
-
-// The instance used: 4 waves x 32 rows per wave -> 128-row q-tiles, 64-key k-tiles.
-constexpr int kNW = 4, kQB = 1;
+// The instance used: 4 waves x 32 query rows -> 128-row q-tiles, 64-key k-tiles.
+constexpr int kNW = 4;
 
 }  // namespace
 
 void flash_tiles(int32_t *tile_m, int32_t *tile_n) {
-    *tile_m = kNW * 32 * kQB;
+    *tile_m = kNW * 32;
     *tile_n = kBN;
 }
 
 hipError_t launch_flash_attention(const FlashLaunch &a, hipStream_t s) {
     const int total = a.H * a.nqt;
     const int per_xcd = (total + 7) / 8;
-    flash_fwd_kernel<kNW, kQB><<<8 * per_xcd, kNW * 64, 4 * a.nkt, s>>>(a);
+    flash_fwd_kernel<kNW><<<8 * per_xcd, kNW * 64, 4 * a.nkt, s>>>(a);
     return hipGetLastError();
 }
 
