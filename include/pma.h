@@ -211,6 +211,103 @@ pma_status pma_attention(const pma_attn_params *p, const pma_layout *layout,
                          const float *k_norm_weight, pma_bf16 *o, int64_t o_ld, float *lse,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+
+/* ======================================================================
+ * 3. DiT block: AdaLN table, LN + modulate, projections, SwiGLU FFN
+ * ----------------------------------------------------------------------
+ * [H3] intro: one block stack over the packed sequence; modality-specific
+ * behaviour comes only from the per-row modality tag selecting the AdaLN
+ * modulation; the block stack is stored in bf16.  [H3] constructor
+ * parameters: hidden_size (5376), ffn_dim (14336) of the SwiGLU feed-forward,
+ * time_embed_dim (2688) = the input of every AdaLN projection, norm_eps
+ * (1e-5) of the pre-attention and pre-feed-forward norms.  [ENG] "Exacte DiT
+ * fusions": the gated residual is written as exact bf16 and the same row is
+ * normalised for the next sublayer; "Profiling en diagnostische pads":
+ * fc1 -> SwiGLU -> fc2.
+ *
+ * Readings of the pages' open points:
+ *   table[g][t][k][c] = sum_e temb[t][e] * W_ada[g][k*hidden + c][e] (per
+ *     tag g in {0 video, 1 text, 2 audio}; no bias, no activation), chunks
+ *     k = 0..5: shift_a, scale_a, gate_a, shift_f, scale_f, gate_f;
+ *   padding rows (tag -1) use all-zero modulation;
+ *   a  = LN(x)  * (1 + scale_a) + shift_a      LN: no affine, population var
+ *   [Q|K|V] = a W_qkv^T                         (attention path of section 2)
+ *   x1 = x  + gate_a * (O W_o^T)
+ *   b  = LN(x1) * (1 + scale_f) + shift_f
+ *   h  = silu(b W_gate^T) * (b W_up^T)          W_fc1 rows = [gate | up]
+ *   x2 = x1 + gate_f * (h W_fc2^T)
+ * Weights are stored [out][in] (row j = the input weights of output j).
+ * ====================================================================== */
+
+typedef struct {
+    int32_t hidden;          /* residual width; multiple of 256              */
+    int32_t ffn_dim;         /* SwiGLU inner width; multiple of 128          */
+    int32_t time_embed_dim;  /* E; multiple of 8                              */
+    float norm_eps;          /* pre-norm epsilon                              */
+    pma_attn_params attn;    /* num_heads * 128 must be a multiple of 256     */
+} pma_block_params;
+
+typedef struct {
+    const pma_bf16 *w_ada;          /* [3][6*hidden][E]                     */
+    const pma_bf16 *w_qkv;          /* [3*H*D][hidden]  Q heads | K | V      */
+    const pma_bf16 *w_o;            /* [hidden][H*D]                         */
+    const pma_bf16 *w_fc1;          /* [2*ffn][hidden]  gate rows | up rows  */
+    const pma_bf16 *w_fc2;          /* [hidden][ffn]                         */
+    const float *q_norm_weight;     /* [128]                                 */
+    const float *k_norm_weight;     /* [128]                                 */
+} pma_block_weights;
+
+/* AdaLN modulation table.  temb: bf16 [T][E]; w_ada: bf16 [3][6*hidden][E];
+ * table: fp32 [3][T][6][hidden].  T <= 8 and T * E <= 24576. */
+pma_status pma_adaln_table(const pma_block_params *p, int32_t num_timesteps,
+                           const pma_bf16 *temb, const pma_bf16 *w_ada, float *table,
+                           void *stream);
+
+/* out = LN(x) * (1 + scale) + shift per row, (shift, scale) gathered from
+ * table by the row's (tag, timestep index); which = 0 selects chunks
+ * (shift_a, scale_a), 1 selects (shift_f, scale_f).  x, out: bf16 [L][hidden]
+ * (may alias). */
+pma_status pma_ln_modulate(const pma_block_params *p, const pma_layout *layout,
+                           const float *table, int32_t which, const pma_bf16 *x,
+                           pma_bf16 *out, void *stream);
+
+/* Epilogues of pma_linear. */
+#define PMA_EPI_STORE         0 /* C = acc                                          */
+#define PMA_EPI_GATE_RESIDUAL 1 /* C = R + gate * acc, gate = table chunk per row    */
+#define PMA_EPI_SWIGLU        2 /* C[:, j] = silu(acc_gate[j]) * acc_up[j]           */
+
+typedef struct {
+    int32_t M;             /* rows of A and C                                        */
+    int32_t N;             /* output columns (SWIGLU: columns of C = gate rows of W) */
+    int32_t K;             /* reduction length; multiple of 64                       */
+    const pma_bf16 *A; int64_t lda;    /* [M][K]                                    */
+    const pma_bf16 *W; int64_t ldw;    /* [N][K]; SWIGLU: [2N][K], up rows at N..2N */
+    pma_bf16 *C; int64_t ldc;          /* [M][N]                                    */
+    int32_t epilogue;      /* PMA_EPI_*                                              */
+    /* GATE_RESIDUAL only: */
+    const pma_bf16 *R; int64_t ldr;    /* residual [M][N] (may alias C)             */
+    const float *table;    /* [3][T][6][N] modulation table                          */
+    int32_t num_timesteps; /* T                                                       */
+    int32_t gate_chunk;    /* 2 (gate_a) or 5 (gate_f)                               */
+    const int32_t *token_tags, *timestep_indices;   /* [M] per-row gather keys      */
+} pma_linear_args;
+
+/* C = epilogue(A W^T) in bf16 with fp32 accumulation on bf16 MFMA.
+ * N % 256 == 0 (SWIGLU: N % 128 == 0), K % 64 == 0, lda/ldw/ldc/ldr % 8 == 0,
+ * pointers 16-byte aligned, M * lda and the rows of W addressable in 32-bit
+ * byte offsets (< 4 GiB).  Rows >= M are neither read nor written. */
+pma_status pma_linear(const pma_linear_args *args, void *stream);
+
+/* Device workspace of pma_block_forward for L rows. */
+pma_status pma_block_workspace_size(const pma_block_params *p, int32_t seq_len, size_t *bytes);
+
+/* One DiT block: x_out = block(x_in).  table from pma_adaln_table; layout
+ * built with the attention tiles.  x_in, x_out: bf16 [L][hidden], distinct. */
+pma_status pma_block_forward(const pma_block_params *p, const pma_layout *layout,
+                             const pma_block_weights *w, const float *table,
+                             const pma_bf16 *x_in, pma_bf16 *x_out, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

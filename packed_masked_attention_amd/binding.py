@@ -54,6 +54,25 @@ class AttnParams(ctypes.Structure):
                 ("softmax_scale", ctypes.c_float)]
 
 
+class BlockParams(ctypes.Structure):
+    _fields_ = [("hidden", _i32), ("ffn_dim", _i32), ("time_embed_dim", _i32),
+                ("norm_eps", ctypes.c_float), ("attn", AttnParams)]
+
+
+class BlockWeights(ctypes.Structure):
+    _fields_ = [("w_ada", _vp), ("w_qkv", _vp), ("w_o", _vp), ("w_fc1", _vp), ("w_fc2", _vp),
+                ("q_norm_weight", _vp), ("k_norm_weight", _vp)]
+
+
+class LinearArgs(ctypes.Structure):
+    _fields_ = [("M", _i32), ("N", _i32), ("K", _i32), ("A", _vp), ("lda", _i64), ("W", _vp),
+                ("ldw", _i64), ("C", _vp), ("ldc", _i64), ("epilogue", _i32), ("R", _vp),
+                ("ldr", _i64), ("table", _vp), ("num_timesteps", _i32), ("gate_chunk", _i32),
+                ("token_tags", _vp), ("timestep_indices", _vp)]
+
+
+EPI_STORE, EPI_GATE_RESIDUAL, EPI_SWIGLU = 0, 1, 2
+
 _SIGS = {
     "pma_status_string": (ctypes.c_char_p, [_i32]),
     "pma_last_error": (ctypes.c_char_p, []),
@@ -74,6 +93,15 @@ _SIGS = {
     "pma_attention": (_i32, [ctypes.POINTER(AttnParams), ctypes.POINTER(Layout), _vp, _i64, _vp,
                              _i64, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, ctypes.c_size_t,
                              _vp]),
+    "pma_adaln_table": (_i32, [ctypes.POINTER(BlockParams), _i32, _vp, _vp, _vp, _vp]),
+    "pma_ln_modulate": (_i32, [ctypes.POINTER(BlockParams), ctypes.POINTER(Layout), _vp, _i32,
+                               _vp, _vp, _vp]),
+    "pma_linear": (_i32, [ctypes.POINTER(LinearArgs), _vp]),
+    "pma_block_workspace_size": (_i32, [ctypes.POINTER(BlockParams), _i32,
+                                        ctypes.POINTER(ctypes.c_size_t)]),
+    "pma_block_forward": (_i32, [ctypes.POINTER(BlockParams), ctypes.POINTER(Layout),
+                                 ctypes.POINTER(BlockWeights), _vp, _vp, _vp, _vp,
+                                 ctypes.c_size_t, _vp]),
 }
 
 _lib = None
@@ -247,3 +275,45 @@ def pma_attention(p: AttnParams, dl: DeviceLayout, q, q_ld, k, k_ld, v, v_ld, wq
     check(lib().pma_attention(ctypes.byref(p), ctypes.byref(dl.struct), ptr(q), q_ld, ptr(k),
                               k_ld, ptr(v), v_ld, ptr(wq), ptr(wk), ptr(o), o_ld, ptr(lse),
                               ptr(workspace), workspace.numel(), stream_ptr(stream)))
+
+
+# ------------------------------------------------------------------- block
+
+def block_params(hidden: int, ffn: int, temb_dim: int, H: int, eps: float = 1e-5,
+                 **attn) -> BlockParams:
+    return BlockParams(hidden, ffn, temb_dim, eps, attn_params(H, **attn))
+
+
+def pma_adaln_table(p: BlockParams, num_timesteps: int, temb, w_ada, table, stream=None) -> None:
+    check(lib().pma_adaln_table(ctypes.byref(p), num_timesteps, ptr(temb), ptr(w_ada), ptr(table),
+                                stream_ptr(stream)))
+
+
+def pma_ln_modulate(p: BlockParams, dl: DeviceLayout, table, which: int, x, out,
+                    stream=None) -> None:
+    check(lib().pma_ln_modulate(ctypes.byref(p), ctypes.byref(dl.struct), ptr(table), which,
+                                ptr(x), ptr(out), stream_ptr(stream)))
+
+
+def pma_linear(M, N, K, A, lda, W, ldw, C, ldc, epilogue=EPI_STORE, R=None, ldr=0, table=None,
+               num_timesteps=1, gate_chunk=0, tags=None, ts_idx=None, stream=None) -> None:
+    args = LinearArgs(M, N, K, ptr(A), lda, ptr(W), ldw, ptr(C), ldc, epilogue, ptr(R), ldr,
+                      ptr(table), num_timesteps, gate_chunk, ptr(tags), ptr(ts_idx))
+    check(lib().pma_linear(ctypes.byref(args), stream_ptr(stream)))
+
+
+def pma_block_workspace_size(p: BlockParams, seq_len: int) -> int:
+    n = ctypes.c_size_t()
+    check(lib().pma_block_workspace_size(ctypes.byref(p), seq_len, ctypes.byref(n)))
+    return n.value
+
+
+def pma_block_forward(p: BlockParams, dl: DeviceLayout, w: BlockWeights, table, x_in, x_out,
+                      workspace=None, stream=None) -> None:
+    import torch
+    nbytes = pma_block_workspace_size(p, dl.seq_len)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x_in.device)
+    check(lib().pma_block_forward(ctypes.byref(p), ctypes.byref(dl.struct), ctypes.byref(w),
+                                  ptr(table), ptr(x_in), ptr(x_out), ptr(workspace),
+                                  workspace.numel(), stream_ptr(stream)))

@@ -117,6 +117,18 @@ pma_status check_tok_major(const char *name, const pma_bf16 *x, int64_t ld, int3
 
 }  // namespace
 
+namespace pma {
+pma_status api_fail(pma_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+pma_status api_check_device() { return check_device(); }
+pma_status api_check_attn_params(const pma_attn_params *p) { return check_attn_params(p); }
+}  // namespace pma
+
 extern "C" {
 
 const char *pma_status_string(pma_status s) {

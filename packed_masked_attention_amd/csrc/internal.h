@@ -73,4 +73,42 @@ struct FlashLaunch {
 void flash_tiles(int32_t *tile_m, int32_t *tile_n);
 hipError_t launch_flash_attention(const FlashLaunch &a, hipStream_t s);
 
+// ------------------------------------------------------------------ block
+struct GemmLaunch {
+    int32_t M, N, K;
+    const uint16_t *A;
+    int64_t lda;
+    const uint16_t *W;
+    int64_t ldw;
+    uint32_t w_bytes;  // bytes of W addressable by the kernel's buffer resource
+    uint16_t *C;
+    int64_t ldc;
+    int32_t epi;
+    const uint16_t *R;
+    int64_t ldr;
+    const float *table;
+    int32_t T, gate_chunk;
+    const int32_t *tags, *ts_idx;
+};
+hipError_t launch_gemm(const GemmLaunch &a, hipStream_t s);
+
+struct LnModLaunch {
+    int32_t L, hidden, T, shift_chunk;
+    float eps;
+    const uint16_t *x;
+    uint16_t *out;
+    const float *table;
+    const int32_t *tags, *ts_idx;
+};
+hipError_t launch_ln_modulate(const LnModLaunch &a, hipStream_t s);
+int ln_modulate_max_hidden();
+
+struct AdaLnLaunch {
+    int32_t T, E, hidden;
+    const uint16_t *temb, *w;
+    float *table;
+};
+hipError_t launch_adaln_table(const AdaLnLaunch &a, hipStream_t s);
+int adaln_max_t();
+
 }  // namespace pma

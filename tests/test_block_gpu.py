@@ -1,0 +1,270 @@
+"""The DiT block on the GPU (through the C ABI) vs the CPU oracle.
+
+Tolerances.  Every GPU stage stores bf16 and accumulates in fp32; the oracle
+in storage mode rounds the same tensors to bf16 and computes the rest in
+fp64.  Stage by stage (test_block_stages_full_size) each GPU stage is within
+one bf16 rounding of the oracle's stage applied to the GPU's own input.
+End to end the two chains drift: the attention's bf16 probabilities move the
+pre-rounding x1 by ~1e-4, flipping about 1% of x1 elements by one ulp, and
+the SwiGLU feed-forward's Jacobian (gain ~15 per unit of its input) spreads
+each flip over every output.  Block outputs are therefore compared on
+(gpu - ref) / rms(ref): mean <= 2e-3 (the target's mean bound, relative to
+the output scale) and max <= 6e-2 or one bf16 ulp of ref (at L=8192 the
+largest outputs exceed 64, where one ulp is 0.5 = 4.2% of rms).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import block as oblock
+from packed_masked_attention_amd import synth
+from tests.helpers import bf16_to_np, say, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _small_inputs(seed=3, L=300, hidden=256, H=2, ffn=512, E=64, pad=20, T=2, std=0.05):
+    rng = np.random.default_rng(seed)
+    tags = rng.integers(0, 3, L).astype(np.int32)
+    tags[L - pad:] = -1
+    pos = rng.integers(0, 50, (L, 3)).astype(np.int32)
+    pos[tags == -1] = 0
+    ts = rng.integers(0, T, L).astype(np.int32)
+    ts[tags == -1] = 0
+    lay = synth.layout_from_tags(tags, pos, ts, T)
+    return synth.make_block_inputs(L, hidden, H, 128, ffn, E, T=T, seed=seed, layout=lay,
+                                   weight_std=std)
+
+
+class BlockRun:
+    def __init__(self, inp, device="cuda"):
+        import torch
+        from packed_masked_attention_amd import binding as B
+        self.B, self.inp = B, inp
+        L, hid, H, ffn, E = inp["L"], inp["hidden"], inp["heads"], inp["ffn"], inp["temb_dim"]
+        self.L, self.hid, self.H, self.ffn, self.E = L, hid, H, ffn, E
+        self.T = inp["layout"]["T"]
+        self.p = B.block_params(hid, ffn, E, H)
+        self.dl = B.pma_layout_build(inp["layout"], device=device)
+        d = lambda k: to_dev_bf16(inp[k], device)
+        self.x, self.temb = d("x"), d("temb")
+        self.w_ada, self.w_qkv, self.w_o = d("w_ada"), d("w_qkv"), d("w_o")
+        self.w_fc1, self.w_fc2 = d("w_fc1"), d("w_fc2")
+        self.qn = torch.ones(128, dtype=torch.float32, device=device)
+        self.kn = torch.ones(128, dtype=torch.float32, device=device)
+        self.table = torch.empty(3, self.T, 6, hid, dtype=torch.float32, device=device)
+        self.w = B.BlockWeights(self.w_ada.data_ptr(), self.w_qkv.data_ptr(), self.w_o.data_ptr(),
+                                self.w_fc1.data_ptr(), self.w_fc2.data_ptr(),
+                                self.qn.data_ptr(), self.kn.data_ptr())
+        self.out = torch.full_like(self.x, float("nan"))
+
+    def adaln(self):
+        self.B.pma_adaln_table(self.p, self.T, self.temb, self.w_ada, self.table)
+
+    def forward(self):
+        import torch
+        self.B.pma_block_forward(self.p, self.dl, self.w, self.table, self.x, self.out)
+        torch.cuda.synchronize()
+        return bf16_to_np(self.out)
+
+
+def _block_close(got, ref, what, mean_rel=2e-3, max_rel=6e-2):
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = np.abs(got - ref)
+    ulp = np.maximum(np.abs(ref), 2.0 ** -126) * 2.0 ** -7
+    over = err > np.maximum(max_rel * rms, ulp)
+    st = {"rms": rms, "max_rel": float(err.max() / rms), "mean_rel": float(err.mean() / rms),
+          "n_over": int(over.sum())}
+    say(f"  {what}: {st}")
+    assert np.all(np.isfinite(got)), what
+    assert st["mean_rel"] <= mean_rel, (what, st)
+    assert not over.any(), (what, st)
+
+
+def test_adaln_table_matches_oracle():
+    inp = _small_inputs()
+    say("adaln table")
+    r = BlockRun(inp)
+    r.adaln()
+    got = r.table.cpu().numpy()
+    ref = oblock.adaln_table(inp["temb"], inp["w_ada"])
+    assert np.allclose(got, ref, rtol=1e-5, atol=1e-5 * np.abs(ref).max())
+
+
+def test_ln_modulate_matches_oracle():
+    import torch
+    inp = _small_inputs(seed=4)
+    say("ln modulate")
+    r = BlockRun(inp)
+    r.adaln()
+    lay = inp["layout"]
+    mod = r.table.cpu().numpy().astype(np.float64)
+    x = oracle.bf16_to_f64(inp["x"])
+    for which, name in ((0, "a"), (1, "f")):
+        out = torch.empty_like(r.x)
+        r.B.pma_ln_modulate(r.p, r.dl, r.table, which, r.x, out)
+        torch.cuda.synchronize()
+        got = bf16_to_np(out)
+        ref = oblock.ln_modulate(x, mod, lay["tags"], lay["ts_idx"], name, 1e-5)
+        bound = np.abs(ref) * 2.0 ** -8 * 1.02 + 1e-5 * np.abs(ref).max()
+        assert np.all(np.abs(got - ref) <= bound), name
+    # x == 0: LN is 0, so the output is the gathered shift exactly (rounded to bf16)
+    zeros = torch.zeros_like(r.x)
+    out = torch.empty_like(r.x)
+    r.B.pma_ln_modulate(r.p, r.dl, r.table, 0, zeros, out)
+    torch.cuda.synchronize()
+    shift = oblock.row_modulation(mod, lay["tags"], lay["ts_idx"], 0)
+    assert np.array_equal(bf16_to_np(out), oracle.bf16_storage(shift))
+
+
+@pytest.mark.parametrize("epi", [0, 1, 2])
+@pytest.mark.parametrize("M", [300, 512])
+def test_linear_epilogues_match_numpy(epi, M):
+    import torch
+    from packed_masked_attention_amd import binding as B
+    rng = np.random.default_rng(10 + epi)
+    N, K, T = 512, 320, 2
+    say(f"linear epi={epi} M={M} N={N} K={K}")
+    A = synth.normal_bf16(rng, (M, K))
+    W = synth.normal_bf16(rng, (2 * N if epi == 2 else N, K), 0.05)
+    Rr = synth.normal_bf16(rng, (M, N))
+    table = rng.standard_normal((3, T, 6, N)).astype(np.float32)
+    tags = rng.integers(-1, 3, M).astype(np.int32)
+    ts = rng.integers(0, T, M).astype(np.int32)
+    dA, dW, dR = to_dev_bf16(A), to_dev_bf16(W), to_dev_bf16(Rr)
+    dC = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dt = torch.from_numpy(table).cuda()
+    dtags, dts = torch.from_numpy(tags).cuda(), torch.from_numpy(ts).cuda()
+    B.pma_linear(M, N, K, dA, K, dW, K, dC, N, epi, R=dR, ldr=N, table=dt, num_timesteps=T,
+                 gate_chunk=2, tags=dtags, ts_idx=dts)
+    torch.cuda.synchronize()
+    got = bf16_to_np(dC)
+    acc = oracle.bf16_to_f64(A) @ oracle.bf16_to_f64(W).T
+    if epi == 0:
+        ref = acc
+    elif epi == 1:
+        gate = np.zeros((M, N))
+        real = tags >= 0
+        gate[real] = table[tags[real], ts[real], 2].astype(np.float64)
+        ref = oracle.bf16_to_f64(Rr) + gate * acc
+    else:
+        ref = oblock.silu(acc[:, :N]) * acc[:, N:]
+    err = np.abs(got - ref)
+    bound = np.abs(ref) * 2.0 ** -8 * 1.02 + 2e-3 * np.sqrt(np.mean(ref ** 2))
+    bad = err > bound
+    assert not bad.any(), f"{int(bad.sum())} values off; worst {err.max()}"
+
+
+def test_block_small_matches_oracle():
+    inp = _small_inputs(seed=5)
+    say("block small: L=300 hidden=256 H=2 ffn=512, 20 padding rows, T=2")
+    r = BlockRun(inp)
+    r.adaln()
+    got = r.forward()
+    mod = r.table.cpu().numpy().astype(np.float64)   # same table on both sides
+    ref = oblock.block_forward(inp, mod=mod)
+    _block_close(got, ref, "block small")
+
+
+def test_block_zero_gates_identity():
+    import torch
+    inp = _small_inputs(seed=6)
+    say("block with zero gates is the identity, bit for bit")
+    r = BlockRun(inp)
+    r.adaln()
+    r.table[:, :, 2] = 0
+    r.table[:, :, 5] = 0
+    got = r.forward()
+    assert np.array_equal(got, oracle.bf16_to_f64(inp["x"]))
+    out1 = r.out.clone()
+    r.forward()
+    assert torch.equal(out1.view(torch.int16), r.out.view(torch.int16)), "not deterministic"
+
+
+def test_block_full_size_sampled_rows():
+    wl = synth.workload("block_L8192")
+    say("block L=8192 hidden=5376 H=56 ffn=14336: generating inputs")
+    inp = synth.make_block_workload(wl)
+    r = BlockRun(inp)
+    r.adaln()
+    got = r.forward()
+    rows = np.sort(np.random.default_rng(7).choice(wl.L, 24, replace=False))
+    say(f"  oracle on {rows.size} sampled rows")
+    mod = r.table.cpu().numpy().astype(np.float64)
+    ref_mod = oblock.adaln_table(inp["temb"], inp["w_ada"])
+    assert np.allclose(mod, ref_mod, rtol=1e-4, atol=1e-4 * np.abs(ref_mod).max())
+    ref = oblock.block_forward(inp, rows=rows, mod=mod)
+    _block_close(got[rows], ref, "block L8192 sampled rows")
+
+
+def test_block_stages_full_size():
+    """Each stage of the L=8192 block, run through the C ABI, against the
+    oracle's same stage fed with the GPU's own input to that stage (sampled
+    rows), so an error is attributed to the stage that makes it."""
+    import torch
+    from packed_masked_attention_amd import binding as B
+    wl = synth.workload("block_L8192")
+    say("block stages L=8192: generating inputs")
+    inp = synth.make_block_workload(wl)
+    r = BlockRun(inp)
+    r.adaln()
+    L, hid, H, ffn = wl.L, wl.hidden, wl.H, wl.ffn
+    HD = H * 128
+    lay = inp["layout"]
+    tags, ts = lay["tags"], lay["ts_idx"]
+    mod = r.table.cpu().numpy().astype(np.float64)
+    rows = np.sort(np.random.default_rng(8).choice(L, 16, replace=False))
+    dev = lambda shape: torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    f64 = lambda t: bf16_to_np(t)
+    stats = {}
+
+    def stage(name, got, ref, rel=2.0 ** -8 * 1.02, floor=2e-3):
+        err = np.abs(got - ref)
+        rms = float(np.sqrt(np.mean(ref ** 2)))
+        bound = np.abs(ref) * rel + floor * rms
+        stats[name] = {"max_rel": float(err.max() / rms), "mean_rel": float(err.mean() / rms),
+                       "n_over": int((err > bound).sum())}
+        say(f"  {name}: {stats[name]}")
+
+    a = dev((L, hid))
+    B.pma_ln_modulate(r.p, r.dl, r.table, 0, r.x, a)
+    qkv = dev((L, 3 * HD))
+    B.pma_linear(L, 3 * HD, hid, a, hid, r.w_qkv, hid, qkv, 3 * HD, 0)
+    o = dev((L, HD))
+    B.pma_attention(r.p.attn, r.dl, qkv, 3 * HD, qkv[:, HD:], 3 * HD, qkv[:, 2 * HD:], 3 * HD,
+                    r.qn, r.kn, o, HD)
+    x1 = dev((L, hid))
+    B.pma_linear(L, hid, HD, o, HD, r.w_o, HD, x1, hid, 1, R=r.x, ldr=hid, table=r.table,
+                 num_timesteps=1, gate_chunk=2, tags=r.dl.arrays["tags"],
+                 ts_idx=r.dl.arrays["ts_idx"])
+    b = dev((L, hid))
+    B.pma_ln_modulate(r.p, r.dl, r.table, 1, x1, b)
+    h = dev((L, ffn))
+    B.pma_linear(L, ffn, hid, b, hid, r.w_fc1, hid, h, ffn, 2)
+    x2 = dev((L, hid))
+    B.pma_linear(L, hid, ffn, h, ffn, r.w_fc2, ffn, x2, hid, 1, R=x1, ldr=hid, table=r.table,
+                 num_timesteps=1, gate_chunk=5, tags=r.dl.arrays["tags"],
+                 ts_idx=r.dl.arrays["ts_idx"])
+    torch.cuda.synchronize()
+    x = oracle.bf16_to_f64(inp["x"])
+    a_g, qkv_g, o_g, x1_g, b_g, h_g, x2_g = (f64(t) for t in (a, qkv, o, x1, b, h, x2))
+    stage("a", a_g[rows], oblock.ln_modulate(x[rows], mod, tags[rows], ts[rows], "a", 1e-5))
+    wq = oracle.bf16_to_f64(inp["w_qkv"])
+    stage("qkv", qkv_g[rows], a_g[rows] @ wq.T)
+    q_bits = oracle.bf16_round(qkv_g[:, :HD])
+    k_bits = oracle.bf16_round(qkv_g[:, HD:2 * HD])
+    v_bits = oracle.bf16_round(qkv_g[:, 2 * HD:])
+    o_ref, _ = oracle.attention_path(q_bits, k_bits, v_bits, lay, H, rows=rows,
+                                     store_qk_bf16=True)
+    stage("o", o_g[rows], o_ref.reshape(rows.size, HD), floor=1e-2)
+    gate_a = oblock.row_modulation(mod, tags, ts, oblock.GATE_A)[rows]
+    stage("x1", x1_g[rows], x[rows] + gate_a * (o_g[rows] @ oracle.bf16_to_f64(inp["w_o"]).T))
+    stage("b", b_g[rows], oblock.ln_modulate(x1_g[rows], mod, tags[rows], ts[rows], "f", 1e-5))
+    w1 = oracle.bf16_to_f64(inp["w_fc1"])
+    g_ = b_g[rows] @ w1[:ffn].T
+    u_ = b_g[rows] @ w1[ffn:].T
+    stage("h", h_g[rows], oblock.silu(g_) * u_)
+    gate_f = oblock.row_modulation(mod, tags, ts, oblock.GATE_F)[rows]
+    stage("x2", x2_g[rows], x1_g[rows] + gate_f * (h_g[rows] @ oracle.bf16_to_f64(inp["w_fc2"]).T))
+    bad = {k: v for k, v in stats.items() if v["n_over"]}
+    assert not bad, bad
