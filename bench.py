@@ -13,6 +13,12 @@ is the flash attention kernel alone, timed with HIP events on the stream it is
 launched on; the cpu_baseline object is the CPU oracle's fp32 attention loop
 timed on a bounded sample of query rows on the host cores.
 
+With --workload block_L8192 the step is instead one DiT block forward
+(AdaLN table + LN/modulate + QKV + attention path + O-projection + FFN) at
+L=8192, hidden 5376, ffn 14336; value is the block's algorithmic TFLOP/s and
+the roofline object is the fc1+SwiGLU GEMM (the block's largest kernel) timed
+in its own launches.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--copy-probe BYTES]
 """
@@ -109,6 +115,86 @@ def copy_probe(nbytes: int) -> None:
     print(json.dumps({"copy_probe_bytes": nbytes}))
 
 
+def block_bench(args) -> int:
+    import numpy as np
+    import torch
+    from packed_masked_attention_amd import binding as B
+    from packed_masked_attention_amd import synth
+
+    torch.cuda.set_device(0)
+    wl = synth.workload(args.workload)
+    log(f"[bench] generating {wl.name} inputs")
+    inp = synth.make_block_workload(wl)
+    L, hid, H, ffn, E = wl.L, wl.hidden, wl.H, wl.ffn, wl.temb_dim
+    HD = H * wl.D
+    dev = torch.device("cuda", 0)
+    to_dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev) \
+        .view(torch.bfloat16)
+    x, temb = to_dev(inp["x"]), to_dev(inp["temb"])
+    w_ada, w_qkv, w_o = to_dev(inp["w_ada"]), to_dev(inp["w_qkv"]), to_dev(inp["w_o"])
+    w_fc1, w_fc2 = to_dev(inp["w_fc1"]), to_dev(inp["w_fc2"])
+    ones = torch.ones(wl.D, dtype=torch.float32, device=dev)
+    p = B.block_params(hid, ffn, E, H)
+    dl = B.pma_layout_build(inp["layout"], device=dev)
+    T = inp["layout"]["T"]
+    table = torch.empty(3, T, 6, hid, dtype=torch.float32, device=dev)
+    w = B.BlockWeights(w_ada.data_ptr(), w_qkv.data_ptr(), w_o.data_ptr(), w_fc1.data_ptr(),
+                       w_fc2.data_ptr(), ones.data_ptr(), ones.data_ptr())
+    out = torch.empty_like(x)
+    ws = torch.empty(B.pma_block_workspace_size(p, L), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.pma_adaln_table(p, T, temb, w_ada, table)
+        B.pma_block_forward(p, dl, w, table, x, out, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    attn = attention_flops(inp["layout"]["tags"], H, wl.D)
+    gemm = 2 * L * hid * (3 * HD) + 2 * L * HD * hid + 2 * L * hid * (2 * ffn) + 2 * L * ffn * hid
+    ada = 2 * 3 * 6 * hid * E * T
+    flops = attn + gemm + ada
+    # dominant kernel: fc1 + SwiGLU, in its own launches on this stream
+    bb = torch.empty(L, hid, dtype=torch.bfloat16, device=dev).normal_()
+    hh = torch.empty(L, ffn, dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        B.pma_linear(L, ffn, hid, bb, hid, w_fc1, hid, hh, ffn, B.EPI_SWIGLU)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        B.pma_linear(L, ffn, hid, bb, hid, w_fc1, hid, hh, ffn, B.EPI_SWIGLU)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fc1_ms = e0.elapsed_time(e1) / args.steps
+    fc1_flops = 2 * L * (2 * ffn) * hid
+    achieved = fc1_flops / (fc1_ms * 1e-3) / 1e12
+    value = flops / (ms_step * 1e-3) / 1e12
+    outj = {
+        "metric": "DiT block forward TFLOP/s at L=8192, hidden 5376, 56x128 heads, ffn 14336",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "seq_len": L, "hidden": hid, "heads": H,
+                   "head_dim": wl.D, "ffn_dim": ffn, "time_embed_dim": E,
+                   "algorithmic_flops": flops,
+                   "step": "AdaLN table + one DiT block forward",
+                   "pct_bf16_peak_step": round(100 * value / BF16_PEAK_TFLOPS, 2)},
+        "roofline": {"kernel": "gemm_kernel<SWIGLU> (fc1)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "avg_ms": round(fc1_ms, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(outj), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +214,8 @@ def main() -> int:
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return 0
+    if args.workload.startswith("block"):
+        return block_bench(args)
 
     import numpy as np
     import torch
