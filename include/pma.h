@@ -195,7 +195,9 @@ pma_status pma_qk_norm_rope(const pma_attn_params *p, const pma_layout *layout,
  * apply the document/bounds mask.
  *   o:   bf16 token-major, row i of head h at o[i*o_ld + h*D .. + D), o_ld >= H*D,
  *        o_ld % 8 == 0.  Only rows < L are written.
- *   lse: fp32 [H][L] natural-log sum of exp of the scaled logits (NULL: not written). */
+ *   lse: fp32 [H][L] natural-log sum of exp of the scaled logits (NULL: not written).
+ * The kernel keeps each q-tile's k-tile list in LDS: layouts of more than
+ * 7932 k-tiles (seq_len > 507648) return PMA_ERR_SHAPE. */
 pma_status pma_flash_attention(const pma_attn_params *p, const pma_layout *layout,
                                const pma_bf16 *qh, const pma_bf16 *kh, const pma_bf16 *vt,
                                pma_bf16 *o, int64_t o_ld, float *lse, void *stream);

@@ -297,6 +297,9 @@ pma_status pma_flash_attention(const pma_attn_params *p, const pma_layout *layou
     if (layout->tile_m != tm || layout->tile_n != tn)
         return fail(PMA_ERR_SHAPE, "layout tiles %d x %d, the attention kernel needs %d x %d",
                     layout->tile_m, layout->tile_n, tm, tn);
+    if (layout->num_k_tiles > flash_max_k_tiles())
+        return fail(PMA_ERR_SHAPE, "seq_len %d: the attention kernel takes at most %d k-tiles (%d keys)",
+                    layout->seq_len, flash_max_k_tiles(), flash_max_k_tiles() * tn);
     if (!qh || !kh || !vt) return fail(PMA_ERR_NULL, "qh, kh and vt are required");
     if (!aligned(qh, 16) || !aligned(kh, 16) || !aligned(vt, 16))
         return fail(PMA_ERR_ALIGN, "qh, kh, vt must be 16-byte aligned");

@@ -6,7 +6,7 @@
 // 128 channels.  Computes, per head, O_i = sum_j softmax_j(scale q_i.k_j) v_j
 // over the keys j of row i's document (scale 1/sqrt(128) by default).
 //
-// Design (one workgroup = one head x one tile of BM query rows):
+// Design (one workgroup = one head x one tile of 256 query rows, 8 waves):
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16.  The A operand is a 32-key slab
 //    of K read from LDS, the B operand Q^T lives in registers for the whole
 //    loop.  In the accumulator every lane then holds ONE query row (lane % 32)
@@ -17,26 +17,33 @@
 //    converted to bf16, are the B operand P^T of O^T = V^T P^T with no data
 //    movement, and V^T (pre-transposed by the prep kernel, keys contiguous)
 //    is read from LDS in natural key order as the A operand.
-//  * Online softmax in fp32 with exp2 (log2 e folded into the scale) and a
-//    lazy reference max: a row's reference only moves when its max grows by
-//    more than 2^8 (so p <= 256, exact in fp32/bf16 range), which makes the
-//    O rescale rare.  Row sums by v_dot2 on the bf16 probabilities actually
-//    fed to the PV product.
-//  * Software pipelined: iteration j issues S(j+1) = K(j+1) Q^T in the same
-//    basic block as the softmax of S(j), so the MFMAs of one overlap the VALU
-//    of the other inside a wave; then O += V(j)^T P(j).  The K and V buffers
-//    run one tile apart (K(j+1) and V(j) are resident during iteration j).
-//  * Tiles come from the layout's per-q-tile list of non-EMPTY k-tiles: EMPTY
-//    tiles are never visited; FULL tiles take no mask ops; PARTIAL tiles and
-//    the ragged last k-tile mask by document bit / bounds from two ballots.
-//  * K and V^T tiles are double-buffered in LDS and filled by direct-to-LDS
-//    buffer loads (buffer_load_dwordx4 ... lds) with the tile offset in an
-//    SGPR: the next tiles stream into the idle buffers while the current ones
-//    are consumed, with no staging registers and no per-tile address VALU;
-//    one wait + barrier per tile.  Each wave-instruction fills
-//    1 KB of LDS in lane order, so instead of row padding the 16-byte chunks
-//    of a row are XOR-swizzled (chosen by the global address each lane
-//    fetches), which keeps the MFMA-operand reads bank-conflict-free.
+//  * Ping-pong between two wave groups.  Waves w and w+4 share a SIMD; group
+//    0 (waves 0-3) and group 1 (waves 4-7) alternate, one barrier-separated
+//    phase apart, between an MFMA phase G(t) = {O += V(t-1)^T P(t-1)^T,
+//    S(t) = K(t) Q^T} (32 MFMAs, raised wave priority) and a softmax phase
+//    S(t) (VALU only).  While one wave of a SIMD runs its MFMAs the other runs
+//    its softmax, so matrix and vector units work at the same time; within a
+//    phase nothing waits on the other unit.
+//  * Softmax in fp32 with exp2 (log2 e folded into the scale) and a lazy
+//    reference max: a row's reference only moves when its max grows by more
+//    than 2^8 (so p <= 256), which makes the O rescale rare.  The row max is
+//    four independent max3 chains and the row sum four independent add
+//    chains: the softmax wave has no other wave to hide its latencies behind.
+//  * K, V^T tiles (64 keys) stream through a 4-deep LDS ring filled by
+//    direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds) with the tile
+//    offset in an SGPR.  Every wave issues its share of tile t+3's K and
+//    t+2's V^T at the start of its G(t); phase ends wait for all but the
+//    newest one or two batches, so each batch has three phases to land and
+//    no wave waits for a tile it just requested.  The 64 document ids of a V
+//    tile's keys ride along in the same slot (for the rare masked tile).
+//    Each 1 KB wave-instruction fills LDS in lane order, so instead of row
+//    padding the 16-byte chunks of a row are XOR-swizzled (chosen by the
+//    global address each lane fetches), which keeps the MFMA-operand reads
+//    bank-conflict-free.
+//  * Tiles come from the layout's per-q-tile list of non-EMPTY k-tiles, copied
+//    to LDS (entry = kt | needs_mask << 30): EMPTY tiles are never visited,
+//    FULL tiles take no mask ops, PARTIAL and ragged tiles mask by document /
+//    bounds with two ballots.
 //  * Launch order is XCD-aware: the dispatcher deals workgroups round-robin
 //    to the 8 XCDs, so workgroup b runs item (b % 8) * per_xcd + b / 8 and
 //    each XCD sweeps whole heads, keeping that head's K/V in its own L2.
@@ -48,9 +55,20 @@
 namespace pma {
 namespace {
 
+constexpr int kNW = 8;                     // waves per workgroup
+constexpr int kBM = kNW * 32;              // 256 query rows per workgroup
 constexpr int kBN = 64;                    // keys per tile
 constexpr int kD = kHeadDim;               // 128
 constexpr int kTileElems = kBN * kD;       // 8192 bf16 = 16 KB per K or V^T tile
+constexpr int kKI = 16 / kNW;              // 1 KB LDS-DMA instructions per wave per tile
+constexpr int kNDMA = 2 * kKI + 1;         // DMA instructions per wave per tile (K, V^T, ids)
+constexpr int kReadAhead = 4;              // LDS fragment reads in flight ahead of the MFMAs
+constexpr int kVPre = 4;                   // V fragments read during the softmax phase
+constexpr int kMask = 0x3fffffff;          // list entry -> k-tile index
+// LDS: 4 K slots + 4 V^T slots (each + 64 document ids) + the tile list
+constexpr int kStaticLds = 4 * kTileElems * 2 + 4 * (kTileElems + 2 * kBN) * 2;
+constexpr int kLdsBytes = 160 * 1024;      // per workgroup on gfx950
+static_assert(kKI * kNW == 16, "16 KB tiles split over the waves");
 
 // LDS placement of 16-byte chunk c of a tile row:
 //   K tile   [64 keys][16 chunks]: position c ^ (row & 15)
@@ -63,13 +81,18 @@ typedef __attribute__((address_space(3))) void lds_void;
 // Buffer resource word 3 for raw (untyped) dword loads.
 constexpr int kRsrcFlags = 0x00020000;
 
-// 16 bytes per lane from a buffer straight into LDS: lane l reads
-// base + voff + soff and lands at lds + 16*l.  Kept out of the kernel
-// template: with the builtin written in the template body the host
-// compilation pass drops the kernel's stub.
+// 16 (or 4) bytes per lane from a buffer straight into LDS: lane l reads
+// base + voff + soff and lands at lds + 16*l (4*l); reads past the
+// resource's size return 0.  Kept out of the kernel template: with the
+// builtin written in the template body the host compilation pass drops the
+// kernel's stub.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_void *l, uint32_t voff,
                                       uint32_t soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, lds_void *l, uint32_t voff,
+                                     uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 4, voff, soff, 0, 0);
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcFlags);
@@ -97,25 +120,42 @@ __device__ __forceinline__ float half_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64, 2) void flash_fwd_kernel(FlashLaunch a) {
-    constexpr int BM = NW * 32;
-    constexpr int KI = 16 / NW;   // 1 KB LDS-DMA instructions per wave per tile (K or V^T)
-    static_assert(KI * NW == 16, "16 KB tiles split over the waves");
-    constexpr int kMask = 0x3fffffff;
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
+#define PMA_WAIT_VM(n) \
+    __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+// End of a phase: this wave's LDS reads done and all but its newest n DMA
+// instructions landed, then the workgroup barrier -- a plain s_barrier (asm
+// with a memory clobber, so no memory access moves across it): the release
+// fence of __syncthreads() would wait for every DMA in flight.
+#define PMA_PHASE_END(n)                                                                   \
+    do {                                                                                    \
+        __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (((n) >> 4) << 14));           \
+        asm volatile("s_barrier" ::: "memory");                                            \
+    } while (0)
 
-    // two buffers per operand as four distinct objects, so the compiler can
-    // tell the buffer being streamed into from the one being read
+__global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch a) {
+    // ring slots as distinct objects, so the compiler can tell the slot being
+    // streamed into from the ones being read
     __shared__ __attribute__((aligned(1024))) uint16_t ks0[kTileElems];
     __shared__ __attribute__((aligned(1024))) uint16_t ks1[kTileElems];
-    __shared__ __attribute__((aligned(1024))) uint16_t vs0[kTileElems];
-    __shared__ __attribute__((aligned(1024))) uint16_t vs1[kTileElems];
-    // this q-tile's k-tile list, entry = kt | (needs_mask << 30); dynamic LDS
-    // of 4 * num_k_tiles bytes.  Reading it from LDS inside the loop keeps the
-    // loop free of vector-memory loads that would wait on the tile stream.
+    __shared__ __attribute__((aligned(1024))) uint16_t ks2[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t ks3[kTileElems];
+    // V^T tile, then the document ids of its 64 keys (int32)
+    __shared__ __attribute__((aligned(1024))) uint16_t vs0[kTileElems + 2 * kBN];
+    __shared__ __attribute__((aligned(1024))) uint16_t vs1[kTileElems + 2 * kBN];
+    __shared__ __attribute__((aligned(1024))) uint16_t vs2[kTileElems + 2 * kBN];
+    __shared__ __attribute__((aligned(1024))) uint16_t vs3[kTileElems + 2 * kBN];
+    // this q-tile's k-tile list, entry = kt | (needs_mask << 30), then 4 pad
+    // entries (tile 0) for the lookahead past the end: dynamic LDS of
+    // 4 * (num_k_tiles + 4) bytes.  Reading it from LDS inside the loop keeps
+    // the loop free of vector-memory loads that would wait on the tile stream.
     extern __shared__ int32_t tlist[];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave-uniform by construction; readfirstlane keeps everything derived from
+    // it (LDS-DMA destinations, row offsets) on the scalar unit
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;
     const int l32 = lane & 31, hi = lane >> 5;
 
     // ---- work item (XCD-aware)
@@ -129,89 +169,63 @@ __global__ __launch_bounds__(NW * 64, 2) void flash_fwd_kernel(FlashLaunch a) {
     {
         const int32_t *list = a.list + (int64_t)qt * a.nkt;
         const uint8_t *cls = a.cls + (int64_t)qt * a.nkt;
-        for (int i = tid; i < cnt; i += NW * 64) {
+        for (int i = tid; i < cnt; i += kNW * 64) {
             const int kt = list[i];
             const bool m = cls[kt] != PMA_TILE_FULL || (kt + 1) * kBN > a.L;
             tlist[i] = kt | (m ? (1 << 30) : 0);
         }
+        if (tid < 4) tlist[cnt + tid] = 0;
     }
     __syncthreads();   // the list is read by every wave from here on
+
     const __amdgpu_buffer_rsrc_t krs =
         make_rsrc(a.kh + (int64_t)head * a.Lp * kD, (uint32_t)a.Lp * kD * 2u);
     const __amdgpu_buffer_rsrc_t vrs =
         make_rsrc(a.vt + (int64_t)head * kD * a.Lp, (uint32_t)a.Lp * kD * 2u);
+    // keys past the sequence read as document 0 here; the mask adds the bound
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(a.doc, (uint32_t)a.L * 4u);
 
     // ---- Q^T fragments: lane holds query row l32, channels 16c + 8*hi + [0, 8)
-    const int q0 = qt * BM + wave * 32;
+    const int q0 = qt * kBM + wave * 32;
     bf16x8 qf[8];
     {
         const uint16_t *qrow = a.qh + ((int64_t)head * a.Lp + q0 + l32) * kD + 8 * hi;
 #pragma unroll
         for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * c);
     }
+    const int qrow = q0 + l32;
+    const int dq = (uint32_t)qrow < (uint32_t)a.L ? a.doc[qrow] : 0;
 
     // ---- LDS-DMA lane offsets.  Wave-instruction j of the K tile fills rows
     // 4j..4j+3 (lane l: row 4j + l/16, position l%16); of the V^T tile, rows
     // 8j..8j+7 (lane l: row 8j + l/8, position l%8).  Each lane fetches the
     // chunk the swizzle places at its position; the tile's own offset
     // (kt * 64 keys) is the SGPR offset.
-    uint32_t kvo[KI], vvo[KI];
+    uint32_t kvo[kKI], vvo[kKI];
 #pragma unroll
-    for (int i = 0; i < KI; ++i) {
-        const int j = wave * KI + i;
+    for (int i = 0; i < kKI; ++i) {
+        const int j = wave * kKI + i;
         const int kr = 4 * j + (lane >> 4), kp = lane & 15;
         kvo[i] = 2u * (uint32_t)(kr * kD + 8 * k_pos(kr, kp));
         const int vr = 8 * j + (lane >> 3), vp = lane & 7;
         vvo[i] = 2u * ((uint32_t)vr * (uint32_t)a.Lp + 8u * v_pos(vr, vp));
     }
+    const uint32_t dvo = 4u * (uint32_t)(wave * 8 + (lane & 7));
     auto dma_k = [&](int kt, uint16_t *dst) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < KI; ++i)
-            dma16(krs, (lds_void *)&dst[(wave * KI + i) * 512], kvo[i], (uint32_t)kt * (kBN * kD * 2));
+        for (int i = 0; i < kKI; ++i)
+            dma16(krs, (lds_void *)&dst[(wave * kKI + i) * 512], kvo[i], (uint32_t)kt * (kBN * kD * 2));
     };
+    // V^T tile plus the document ids of its keys (8 per wave: lanes 0..7)
     auto dma_v = [&](int kt, uint16_t *dst) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < KI; ++i)
-            dma16(vrs, (lds_void *)&dst[(wave * KI + i) * 512], vvo[i], (uint32_t)kt * (kBN * 2));
+        for (int i = 0; i < kKI; ++i)
+            dma16(vrs, (lds_void *)&dst[(wave * kKI + i) * 512], vvo[i], (uint32_t)kt * (kBN * 2));
+        if (lane < 8) dma4(drs, (lds_void *)&dst[kTileElems + wave * 16], dvo, (uint32_t)kt * (kBN * 4));
     };
 
-    // ---- S^T = K Q^T over one K tile: two 32-key slabs
     const int krow = k_slab_row(l32);
-    auto qk = [&](const uint16_t *kbuf, f32x16 (&s)[2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
-            const int r = 32 * kb + krow;
-            const uint16_t *kp = kbuf + r * kD;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kp + 8 * k_pos(r, 2 * c + hi));
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
-            }
-        }
-    };
-
-    // ---- document / bounds mask of a PARTIAL or ragged tile
-    const int qrow = q0 + l32;
-    const int dq = (uint32_t)qrow < (uint32_t)a.L ? a.doc[qrow] : 0;
-    auto apply_mask = [&](int kt, f32x16 (&s)[2]) __attribute__((always_inline)) {
-        const int key = kt * kBN + lane;
-        const int dk = (uint32_t)key < (uint32_t)a.L ? a.doc[key] : -1;
-        const uint64_t padm = __ballot(dk == 1), realm = __ballot(dk == 0);
-        const uint64_t allow = dq ? padm : realm;
-        // the lane's 32 keys are the bytes 16g + 8*hi (g = 0..3) of the tile;
-        // gather them so bit 16*kb + v is register (kb, v)
-        const uint32_t lo = (uint32_t)allow, hw = (uint32_t)(allow >> 32);
-        const uint32_t sh = 8u * hi;
-        const uint32_t m32 = ((lo >> sh) & 0xffu) | (((lo >> (16 + sh)) & 0xffu) << 8) |
-                             (((hw >> sh) & 0xffu) << 16) | (((hw >> (16 + sh)) & 0xffu) << 24);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                if (!((m32 >> (16 * kb + v)) & 1u)) s[kb][v] = -INFINITY;
-    };
+    const float c2 = a.scale_log2;
 
     // ---- per-row state: lazy reference max (log2 units), partial row sum, O^T
     float mref = -INFINITY, lsum = 0.f;
@@ -220,51 +234,102 @@ __global__ __launch_bounds__(NW * 64, 2) void flash_fwd_kernel(FlashLaunch a) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
-    const float c2 = a.scale_log2;
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    f32x16 s[2];     // S(t)^T, 2 slabs of 32 keys
+    bf16x8 pf[4];    // P(t)^T in bf16, 4 chunks of 16 keys
+    bf16x8 vpre[kVPre];
 
-    // ---- prologue: K(0), V(0), K(1) resident; S(0) computed and masked
-    f32x16 s[2];
-    {
-        const int e0 = tlist[0];
-        dma_k(e0 & kMask, ks0);
-        dma_v(e0 & kMask, vs0);
-        if (cnt > 1) dma_k(tlist[1] & kMask, ks1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        qk(ks0, s);
-        if (e0 >> 30) apply_mask(e0 & kMask, s);
-        __syncthreads();   // every wave is done with ks0 before it is refilled
-    }
-
-    // iteration j: reads K(j+1) from kr and V(j) from vr; streams K(j+2) into
-    // kw and V(j+1) into vw
-    auto step = [&](int j, const uint16_t *kr, uint16_t *kw, const uint16_t *vr, uint16_t *vw)
-                    __attribute__((always_inline)) {
-        const bool has1 = j + 1 < cnt;
-        const int e1 = has1 ? tlist[j + 1] : 0;
-        if (j + 2 < cnt) dma_k(tlist[j + 2] & kMask, kw);
-        if (has1) dma_v(e1 & kMask, vw);
-
-        // S(j+1): issued unconditionally (a stale buffer past the end is read
-        // and discarded) so it shares a basic block with the softmax below
-        f32x16 sn[2];
-        qk(kr, sn);
-
-        // softmax of S(j) -> P(j)^T in bf16
-        float mx = s[0][0];
+    // ---- MFMA phase: O^T += V(t-1)^T P(t-1)^T (when withpv), S(t) = K(t) Q^T
+    auto gphase = [&](bool withpv, const uint16_t *vr, const uint16_t *kr) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_setprio(1);
+        if (withpv) {
+            // channel blocks interleaved so consecutive MFMAs are independent
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+                for (int db = 0; db < 4; ++db) {
+                    const int d = 32 * db + l32;
+                    const int f = cc * 4 + db;
+                    const bf16x8 vf = f < kVPre ? vpre[f < kVPre ? f : 0]
+                                                : *reinterpret_cast<const bf16x8 *>(vr + d * kBN + 8 * v_pos(d, 2 * cc + hi));
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[cc], o[db], 0, 0, 0);
+                }
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+            for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int r = 32 * kb + krow;
+                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kr + r * kD + 8 * k_pos(r, 2 * c + hi));
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
+            }
+        // LDS fragment reads run kReadAhead ahead of their MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    // ---- softmax phase of tile t (list entry e, V(t) slot vn): mask,
+    // lazy-max softmax -> P(t)^T in bf16, O rescale
+    auto sphase = [&](int e, const uint16_t *vn) __attribute__((always_inline)) {
+        // V(t) fragments for the first MFMAs of the next PV, read while the
+        // softmax runs
+#pragma unroll
+        for (int f = 0; f < kVPre; ++f) {
+            const int cc = f / 4, db = f % 4;
+            const int d = 32 * db + l32;
+            vpre[f] = *reinterpret_cast<const bf16x8 *>(vn + d * kBN + 8 * v_pos(d, 2 * cc + hi));
+        }
+        if (e >> 30) {
+            // document / bounds mask of a PARTIAL or ragged tile.  The lane's
+            // 32 keys are the bytes 16g + 8*hi (g = 0..3) of the tile's
+            // ballot; gather them so bit 16*kb + v is register (kb, v)
+            const int key = (e & kMask) * kBN + lane;
+            const int dk = (uint32_t)key < (uint32_t)a.L
+                               ? reinterpret_cast<const int32_t *>(vn + kTileElems)[lane] : -1;
+            // both ballots over the whole wave (lane = key), then the row's pick:
+            // a ballot under a divergent select would drop the other lanes' keys
+            const uint64_t padm = __ballot(dk == 1), realm = __ballot(dk == 0);
+            const uint64_t allow = dq ? padm : realm;
+            const uint32_t lo = (uint32_t)allow, hw = (uint32_t)(allow >> 32);
+            const uint32_t sh = 8u * hi;
+            const uint32_t m32 = ((lo >> sh) & 0xffu) | (((lo >> (16 + sh)) & 0xffu) << 8) |
+                                 (((hw >> sh) & 0xffu) << 16) | (((hw >> (16 + sh)) & 0xffu) << 24);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    if (!((m32 >> (16 * kb + v)) & 1u)) s[kb][v] = -INFINITY;
+        }
+        // row max over four independent max3 chains (the three-input form
+        // takes the raw MFMA results; a tree of two-input maxima would first
+        // canonicalize every leaf)
+        float m4[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int b = 8 * (g & 1);
+            float m = fmaxf(s[g >> 1][b], s[g >> 1][b + 1]);
+#pragma unroll
+            for (int k = 2; k < 8; k += 2) m = fmaxf(fmaxf(m, s[g >> 1][b + k]), s[g >> 1][b + k + 1]);
+            m4[g] = m;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(m4[0], m4[1]), m4[2]), m4[3]);
         mx = half_max(mx) * c2;
         const bool need = mx > mref + 8.0f;
         const float mnew = need ? mx : mref;
         const float alpha = need ? __builtin_amdgcn_exp2f(mref - mnew) : 1.0f;
         mref = mnew;
         const float mu = (mnew == -INFINITY) ? 0.f : mnew;
-        float rs = 0.f;
-        bf16x8 pf[4];
+        // probabilities; the row sum (four independent chains) is taken over
+        // the fp32 values before their rounding to bf16
+        float rsp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
             bf16x2 pp[4];
@@ -274,52 +339,97 @@ __global__ __launch_bounds__(NW * 64, 2) void flash_fwd_kernel(FlashLaunch a) {
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(s[cc >> 1][8 * (cc & 1) + 2 * t + 1], c2, -mu));
                 const f32x2 pv = {p0, p1};
                 pp[t] = __builtin_convertvector(pv, bf16x2);
-                rs = __builtin_amdgcn_fdot2_f32_bf16(pp[t], ones, rs, false);
+                rsp[t] += p0 + p1;
             }
             pf[cc] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
                                              __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
                                              0, 1, 2, 3, 4, 5, 6, 7);
         }
-        lsum = fmaf(lsum, alpha, rs);
-        // interleave S(j+1)'s MFMAs with the softmax VALU: K fragment reads run
-        // two ahead, then 16 x {1 MFMA, 1 LDS read, 6 VALU}
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-        }
-        // the row sum in the condition (never negative) keeps the softmax
-        // above this branch, in the block it shares with S(j+1)'s MFMAs
-        if (__ballot(need || !(rs >= 0.f))) {
+        lsum = fmaf(lsum, alpha, (rsp[0] + rsp[1]) + (rsp[2] + rsp[3]));
+        // keep the softmax in this phase: without a use here the compiler
+        // sinks it past the barrier into the MFMA phase that consumes P
+        asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3]), "v"(lsum));
+        if (__ballot(need)) {
 #pragma unroll
             for (int db = 0; db < 4; ++db) o[db] *= alpha;
         }
-
-        // O^T += V(j)^T P(j)^T
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            const int d = 32 * db + l32;
-            const uint16_t *vp = vr + d * kBN;
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(vp + 8 * v_pos(d, 2 * cc + hi));
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[cc], o[db], 0, 0, 0);
-            }
-        }
-
-        if (has1 && (e1 >> 30)) apply_mask(e1 & kMask, sn);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb] = sn[kb];
-        __builtin_amdgcn_s_waitcnt(0);   // the streamed tiles have landed
-        __syncthreads();
     };
 
-    for (int j = 0; j < cnt; j += 2) {
-        step(j, ks1, ks0, vs0, vs1);
-        if (j + 1 < cnt) step(j + 1, ks0, ks1, vs1, vs0);
+    // ---- prologue: K(0..2), V(0..1) resident
+    dma_k(__builtin_amdgcn_readfirstlane(tlist[0]) & kMask, ks0);
+    dma_k(__builtin_amdgcn_readfirstlane(tlist[1]) & kMask, ks1);
+    dma_k(__builtin_amdgcn_readfirstlane(tlist[2]) & kMask, ks2);
+    dma_v(__builtin_amdgcn_readfirstlane(tlist[0]) & kMask, vs0);
+    dma_v(__builtin_amdgcn_readfirstlane(tlist[1]) & kMask, vs1);
+    PMA_PHASE_END(0);
+
+    // Global phase p: group 0 runs G(t) at p = 2t and S(t) at 2t + 1; group 1
+    // runs one phase later.  Tile x sits in ring slot x % 4.  K(t) is read in
+    // phases 2t, 2t+1; V(t) in 2t+1 .. 2t+3.  Each wave issues its share of
+    // DMA(t) = {K(t+3), V(t+2)} at the start of its G(t) (the slots of K(t-1)
+    // and V(t-2), both done with by the end of phase 2t-1); the waits at
+    // phase ends (two batches may stay in flight after G, one after S) make
+    // DMA(t) land by the end of phase 2t+4, before either tile is first read.
+    if (grp == 1) PMA_PHASE_END(0);
+
+    // list entries of the current tile t: ce = entry t, ck = entry t+3 (the
+    // K tile to fetch), cv = entry t+2 (the V tile to fetch).  The next
+    // tile's are read during the softmax phase, so the MFMA phase starts
+    // without an LDS wait.
+    int ce = __builtin_amdgcn_readfirstlane(tlist[0]);
+    int ck = __builtin_amdgcn_readfirstlane(tlist[3]);
+    int cv = __builtin_amdgcn_readfirstlane(tlist[2]);
+    // k_r = K(t), k_m = slot of K(t-1) <- K(t+3); v_r = V(t), v_p = V(t-1),
+    // v_q = slot of V(t-2) <- V(t+2)
+    auto tile = [&](int t, bool withpv, uint16_t *k_r, uint16_t *k_m, uint16_t *v_r,
+                    uint16_t *v_p, uint16_t *v_q) __attribute__((always_inline)) {
+        const int e = ce;
+        dma_k(ck & kMask, k_m);
+        dma_v(cv & kMask, v_q);
+        gphase(withpv, v_p, k_r);
+        PMA_PHASE_END(2 * kNDMA);
+        const int ne = tlist[t + 1], nk = tlist[t + 4], nv = tlist[t + 3];
+        sphase(e, v_r);
+        ce = __builtin_amdgcn_readfirstlane(ne);
+        ck = __builtin_amdgcn_readfirstlane(nk);
+        cv = __builtin_amdgcn_readfirstlane(nv);
+        PMA_PHASE_END(kNDMA);
+    };
+    //    t, pv,   K(t) K(t-1) V(t) V(t-1) V(t-2)
+    tile(0, false, ks0, ks3, vs0, vs3, vs2);
+    int t = 1;
+    for (; t + 4 <= cnt; t += 4) {
+        tile(t, true, ks1, ks0, vs1, vs0, vs3);
+        tile(t + 1, true, ks2, ks1, vs2, vs1, vs0);
+        tile(t + 2, true, ks3, ks2, vs3, vs2, vs1);
+        tile(t + 3, true, ks0, ks3, vs0, vs3, vs2);
     }
+    // t % 4 == 1 here
+    if (t < cnt) tile(t, true, ks1, ks0, vs1, vs0, vs3), ++t;
+    if (t < cnt) tile(t, true, ks2, ks1, vs2, vs1, vs0), ++t;
+    if (t < cnt) tile(t, true, ks3, ks2, vs3, vs2, vs1), ++t;
+
+    // ---- final PV of the last tile (its V sits in slot (cnt - 1) % 4)
+    {
+        const int r = (cnt - 1) & 3;
+        const uint16_t *vr = r == 0 ? vs0 : (r == 1 ? vs1 : (r == 2 ? vs2 : vs3));
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const int d = 32 * db + l32;
+                const int f = cc * 4 + db;
+                const bf16x8 vf = f < kVPre ? vpre[f < kVPre ? f : 0]
+                                            : *reinterpret_cast<const bf16x8 *>(vr + d * kBN + 8 * v_pos(d, 2 * cc + hi));
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[cc], o[db], 0, 0, 0);
+            }
+        __builtin_amdgcn_s_setprio(0);
+    }
+    // no LDS-DMA may still be writing when the workgroup's LDS is released;
+    // group 0 matches group 1's extra barrier
+    PMA_WAIT_VM(0);
+    if (grp == 0) PMA_PHASE_END(0);
 
     // ---- epilogue: O row = O^T column / row sum; register v of d-block db is
     // channel 32*db + 8*(v/4) + 4*hi + v%4
@@ -341,20 +451,20 @@ __global__ __launch_bounds__(NW * 64, 2) void flash_fwd_kernel(FlashLaunch a) {
     }
 }
 
-// The instance used: 4 waves x 32 query rows -> 128-row q-tiles, 64-key k-tiles.
-constexpr int kNW = 4;
-
 }  // namespace
 
 void flash_tiles(int32_t *tile_m, int32_t *tile_n) {
-    *tile_m = kNW * 32;
+    *tile_m = kBM;
     *tile_n = kBN;
 }
+
+int32_t flash_max_k_tiles() { return (kLdsBytes - kStaticLds) / 4 - 4; }
 
 hipError_t launch_flash_attention(const FlashLaunch &a, hipStream_t s) {
     const int total = a.H * a.nqt;
     const int per_xcd = (total + 7) / 8;
-    flash_fwd_kernel<kNW><<<8 * per_xcd, kNW * 64, 4 * a.nkt, s>>>(a);
+    const size_t dyn = 4 * ((size_t)a.nkt + 4);
+    flash_fwd_kernel<<<8 * per_xcd, kNW * 64, dyn, s>>>(a);
     return hipGetLastError();
 }
 

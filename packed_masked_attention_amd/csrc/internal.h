@@ -71,6 +71,8 @@ struct FlashLaunch {
     const int32_t *count, *list, *order;
 };
 void flash_tiles(int32_t *tile_m, int32_t *tile_n);
+// most k-tiles a layout may have for the attention kernel (its LDS tile list)
+int32_t flash_max_k_tiles();
 hipError_t launch_flash_attention(const FlashLaunch &a, hipStream_t s);
 
 // ------------------------------------------------------------------ block

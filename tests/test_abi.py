@@ -69,3 +69,13 @@ def test_host_side_argument_errors(lib):
     lay = B.Layout()
     assert lib.pma_flash_attention(ctypes.byref(p), ctypes.byref(lay), None, None, None, None, 0,
                                    None, None) == 1
+    # a layout past the kernel's LDS tile-list capacity is refused on the host
+    tm, tn = ctypes.c_int32(), ctypes.c_int32()
+    lib.pma_attention_tiles(ctypes.byref(tm), ctypes.byref(tn))
+    fake = ctypes.c_void_p(256)
+    nk = 7933
+    big = B.Layout(nk * tn.value, 1, tm.value, tn.value, (nk * tn.value + tm.value - 1) // tm.value,
+                   nk, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake)
+    assert lib.pma_flash_attention(ctypes.byref(p), ctypes.byref(big), fake, fake, fake, fake,
+                                   56 * 128, None, None) == 2
+    assert "k-tiles" in lib.pma_last_error().decode()
