@@ -49,6 +49,33 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
+def gpu_state():
+    """Clocks and power of GPU 0 from rocm-smi (a child process), or None when
+    it is unavailable.  Read outside the timed region."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
+                           capture_output=True, text=True, timeout=30)
+        d = json.loads(r.stdout)
+    except Exception:
+        return None
+    card = next((v for k, v in d.items() if k.startswith("card")), None)
+    if not isinstance(card, dict):
+        return None
+    out = {}
+    for key, val in card.items():
+        k, v = key.lower(), str(val)
+        mhz = re.search(r"([0-9.]+)\s*mhz", v, re.IGNORECASE)
+        if mhz and "sclk" in k:
+            out["sclk_mhz"] = float(mhz.group(1))
+        elif mhz and "mclk" in k:
+            out["mclk_mhz"] = float(mhz.group(1))
+        elif "power" in k and "(w)" in k and re.fullmatch(r"\s*[0-9.]+\s*", v):
+            out["power_w"] = float(v)
+    return out or None
+
+
 def attention_flops(tags, H: int, D: int) -> int:
     import numpy as np
     tags = np.asarray(tags)
@@ -198,7 +225,7 @@ def block_bench(args) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="masked_L16384")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -265,14 +292,20 @@ def main() -> int:
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
+    state_before = gpu_state()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    state_after = gpu_state()
     ms_step = wall * 1e3 / args.steps
-    flash_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    per_launch = np.array([a.elapsed_time(b) for a, b in evs])
+    flash_ms = float(per_launch.mean())
+    q25, q50, q75 = (float(x) for x in np.percentile(per_launch, [25, 50, 75]))
+    log(f"[bench] flash per launch: median {q50:.4f} ms, IQR {q25:.4f}-{q75:.4f} ms; "
+        f"gpu before {state_before}, after {state_after}")
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (flash_ms * 1e-3) / 1e12
 
@@ -306,8 +339,10 @@ def main() -> int:
         "roofline": {"kernel": "flash_fwd_kernel", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic_from_profiles(), "avg_ms": round(flash_ms, 4)},
+                     "traffic": traffic_from_profiles(), "avg_ms": round(flash_ms, 4),
+                     "median_ms": round(q50, 4), "iqr_ms": [round(q25, 4), round(q75, 4)]},
         "cpu_baseline": cpu,
+        "gpu_state": {"before": state_before, "after": state_after},
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -15,7 +15,8 @@
 //
 // HBM-bound: per (row, head) it reads 3 x 256 B and writes 3 x 256 B.
 // Block = 64 rows x 4 heads.  Each 16-lane group owns one (row, head) of Q or
-// K, 8 channels (16 bytes) per lane; the sum of squares is reduced across the
+// K, 8 channels (16 bytes) per lane, and keeps four such items' loads in
+// flight before it computes them; the sum of squares is reduced across the
 // group and the RoPE partner channels c +/- F sit F/8 lanes away.  cos/sin of
 // the 64 rows x 3F angles are computed once per block in fp64 (angles reach
 // ~1e3 rad, so no fast-math approximation) and kept in LDS as fp32.  V goes
@@ -71,60 +72,71 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(PrepLaunch a) {
     const int in_sec = chunk % sec_chunks;
     const bool first_half = in_sec < half_chunks;
     const int f0 = (first_half ? in_sec : in_sec - half_chunks) * 8;
-    for (int item = sub; item < n_items; item += kThreads / 16) {
-        const int rl = item % kRows;
-        const int hl = (item / kRows) % nh;
-        const int tensor = item / (kRows * nh);   // 0 = Q, 1 = K
-        const int row = r0 + rl;
-        const int h = h0 + hl;
-        const uint16_t *src = tensor ? a.k : a.q;
-        const int64_t ld = tensor ? a.k_ld : a.q_ld;
-        const float *w = tensor ? a.wk : a.wq;
-        uint16_t *dst = tensor ? a.kh : a.qh;
-
-        float x[8];
-        if (row < a.L) {
-            const u16x8 raw = *reinterpret_cast<const u16x8 *>(src + (int64_t)row * ld +
-                                                               h * kHeadDim + chunk * 8);
+    constexpr int kB = 4;   // items in flight per 16-lane group
+    for (int base = sub; base < n_items; base += kB * (kThreads / 16)) {
+        u16x8 raw[kB];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) x[t] = bf16_bits_to_f32(raw[t]);
-        } else {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) x[t] = 0.f;
+        for (int u = 0; u < kB; ++u) {
+            const int item = base + u * (kThreads / 16);
+            const int rl = item % kRows;
+            const int hl = (item / kRows) % nh;
+            const int tensor = item / (kRows * nh);
+            const int row = r0 + rl;
+            const uint16_t *src = tensor ? a.k : a.q;
+            const int64_t ld = tensor ? a.k_ld : a.q_ld;
+            raw[u] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            if (item < n_items && row < a.L)
+                raw[u] = *reinterpret_cast<const u16x8 *>(src + (int64_t)row * ld +
+                                                          (h0 + hl) * kHeadDim + chunk * 8);
         }
-        float ss = 0.f;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) ss = fmaf(x[t], x[t], ss);
-        ss += __shfl_xor(ss, 1, 16);
-        ss += __shfl_xor(ss, 2, 16);
-        ss += __shfl_xor(ss, 4, 16);
-        ss += __shfl_xor(ss, 8, 16);
-        const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
-        const f32x4 w0 = *reinterpret_cast<const f32x4 *>(w + chunk * 8);
-        const f32x4 w1 = *reinterpret_cast<const f32x4 *>(w + chunk * 8 + 4);
-        float n[8];
-        n[0] = x[0] * r * w0[0]; n[1] = x[1] * r * w0[1];
-        n[2] = x[2] * r * w0[2]; n[3] = x[3] * r * w0[3];
-        n[4] = x[4] * r * w1[0]; n[5] = x[5] * r * w1[1];
-        n[6] = x[6] * r * w1[2]; n[7] = x[7] * r * w1[3];
-        float y[8];
-        // partner channels: chunk +/- F/8 within the 16-lane group
+        for (int u = 0; u < kB; ++u) {
+            const int item = base + u * (kThreads / 16);
+            if (item >= n_items) break;
+            const int rl = item % kRows;
+            const int hl = (item / kRows) % nh;
+            const int tensor = item / (kRows * nh);   // 0 = Q, 1 = K
+            const int row = r0 + rl;
+            const int h = h0 + hl;
+            const float *w = tensor ? a.wk : a.wq;
+            uint16_t *dst = tensor ? a.kh : a.qh;
+            float x[8];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const float pn = __shfl_xor(n[t], half_chunks, 16);
-            if (rotated) {
-                const float2 e = cs[rl][ax * F + f0 + t];
-                y[t] = first_half ? (n[t] * e.x - pn * e.y) : (n[t] * e.x + pn * e.y);
-            } else {
-                y[t] = n[t];
+            for (int t = 0; t < 8; ++t) x[t] = bf16_bits_to_f32(raw[u][t]);
+            float ss = 0.f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) ss = fmaf(x[t], x[t], ss);
+            ss += __shfl_xor(ss, 1, 16);
+            ss += __shfl_xor(ss, 2, 16);
+            ss += __shfl_xor(ss, 4, 16);
+            ss += __shfl_xor(ss, 8, 16);
+            const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
+            const f32x4 w0 = *reinterpret_cast<const f32x4 *>(w + chunk * 8);
+            const f32x4 w1 = *reinterpret_cast<const f32x4 *>(w + chunk * 8 + 4);
+            float n[8];
+            n[0] = x[0] * r * w0[0]; n[1] = x[1] * r * w0[1];
+            n[2] = x[2] * r * w0[2]; n[3] = x[3] * r * w0[3];
+            n[4] = x[4] * r * w1[0]; n[5] = x[5] * r * w1[1];
+            n[6] = x[6] * r * w1[2]; n[7] = x[7] * r * w1[3];
+            float y[8];
+            // partner channels: chunk +/- F/8 within the 16-lane group
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float pn = __shfl_xor(n[t], half_chunks, 16);
+                if (rotated) {
+                    const float2 e = cs[rl][ax * F + f0 + t];
+                    y[t] = first_half ? (n[t] * e.x - pn * e.y) : (n[t] * e.x + pn * e.y);
+                } else {
+                    y[t] = n[t];
+                }
             }
-        }
-        uint32_t packed[4];
+            uint32_t packed[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) packed[t] = pack_bf16x2(y[2 * t], y[2 * t + 1]);
-        uint4 out = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-        if (row >= a.L) out = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4 *>(dst + ((int64_t)h * a.Lp + row) * kHeadDim + chunk * 8) = out;
+            for (int t = 0; t < 4; ++t) packed[t] = pack_bf16x2(y[2 * t], y[2 * t + 1]);
+            uint4 out = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+            if (row >= a.L) out = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(dst + ((int64_t)h * a.Lp + row) * kHeadDim + chunk * 8) = out;
+        }
     }
 
     // ---- V: stage [64 rows][128] per head, write [128 channels][64 rows]
