@@ -300,11 +300,37 @@ typedef struct {
  * byte offsets (< 4 GiB).  Rows >= M are neither read nor written. */
 pma_status pma_linear(const pma_linear_args *args, void *stream);
 
+/* (cos, sin) of every row's rotation angles for the fused QKV projection:
+ * table fp32 [L][3F][2], entry [i][a*F + f] = (cos, sin) of
+ * pos[i][a] * theta^(-f/F) (the angle of the attention section's RoPE),
+ * computed in fp64 and rounded to fp32.  table 8-byte aligned. */
+pma_status pma_rope_table(const pma_attn_params *p, const pma_layout *layout, float *table,
+                          void *stream);
+
+/* The QKV projection fused with QK-RMSNorm + 3-axis RoPE: from a (bf16
+ * [L][hidden], leading dimension lda) and w_qkv ([3*H*D][hidden], Q rows,
+ * then K, then V) it writes the operands pma_qk_norm_rope would write --
+ * qh, kh [H][Lp][D] normalised and rotated, vt [H][D][Lp] -- without storing
+ * Q, K, V: the norm and rotation read the fp32 accumulators (Q and K are
+ * rounded to bf16 once, after rotation).  Rows L..Lp-1 are written as zero.
+ * H must be even (a 256-column tile never straddles Q, K and V); hidden %
+ * 64 == 0; a, w_qkv, qh, kh, vt, the norm weights and rope_table (from
+ * pma_rope_table) 16-byte aligned.
+ * [ENG] "Checkpoint layout en media pipeline": the engine runs the QK
+ * normalisation and RoPE as one fused kernel on the projection output. */
+pma_status pma_qkv_projection(const pma_attn_params *p, const pma_layout *layout,
+                              const pma_bf16 *a, int64_t lda, int32_t hidden,
+                              const pma_bf16 *w_qkv, const float *q_norm_weight,
+                              const float *k_norm_weight, const float *rope_table,
+                              pma_bf16 *qh, pma_bf16 *kh, pma_bf16 *vt, void *stream);
+
 /* Device workspace of pma_block_forward for L rows. */
 pma_status pma_block_workspace_size(const pma_block_params *p, int32_t seq_len, size_t *bytes);
 
 /* One DiT block: x_out = block(x_in).  table from pma_adaln_table; layout
- * built with the attention tiles.  x_in, x_out: bf16 [L][hidden], distinct. */
+ * built with the attention tiles.  x_in, x_out: bf16 [L][hidden], distinct.
+ * The QKV projection is pma_qkv_projection (Q and K are never stored), so
+ * the head count is even. */
 pma_status pma_block_forward(const pma_block_params *p, const pma_layout *layout,
                              const pma_block_weights *w, const float *table,
                              const pma_bf16 *x_in, pma_bf16 *x_out, void *workspace,

@@ -77,8 +77,13 @@ def silu(z):
 def block_forward(inp: dict, rows=None, store_bf16: bool = True, eps: float = 1e-5,
                   qk_eps: float = 1e-5, F: int = 16, theta: float = 10000.0,
                   wq=1.0, wk=1.0, mod: np.ndarray | None = None,
-                  return_intermediates: bool = False):
-    """x2 for the listed rows (all rows when ``rows`` is None)."""
+                  return_intermediates: bool = False, fused_qkv: bool = False):
+    """x2 for the listed rows (all rows when ``rows`` is None).
+
+    ``fused_qkv``: the QKV projection hands its Q and K columns straight to
+    the QK-norm + RoPE (the engine page's fused QK normalisation/RoPE kernel)
+    without storing them, so in storage mode Q and K are not rounded to bf16
+    before the norm (V, Q' and K' still are)."""
     lay = inp["layout"]
     tags, ts = lay["tags"], lay["ts_idx"]
     L, hidden, H, D, ffn = inp["L"], inp["hidden"], inp["heads"], inp["head_dim"], inp["ffn"]
@@ -91,8 +96,10 @@ def block_forward(inp: dict, rows=None, store_bf16: bool = True, eps: float = 1e
     x = bf16_to_f64(inp["x"])                                        # [L, hidden]
     a = st(ln_modulate(x, mod, tags, ts, "a", eps))                  # all rows (K, V)
     w_qkv = bf16_to_f64(inp["w_qkv"])
-    kv = st(a @ w_qkv[HD:].T)                                        # [L, 2*HD]
-    qr = st(a[rows] @ w_qkv[:HD].T)                                  # [n, HD]
+    st_qk = (lambda z: z) if fused_qkv else st
+    kv = a @ w_qkv[HD:].T                                            # [L, 2*HD]
+    kv = np.concatenate([st_qk(kv[:, :HD]), st(kv[:, HD:])], axis=1)
+    qr = st_qk(a[rows] @ w_qkv[:HD].T)                               # [n, HD]
 
     # the attention path on stored bf16 Q, K, V
     q_all = np.zeros((L, HD))

@@ -97,6 +97,9 @@ _SIGS = {
     "pma_ln_modulate": (_i32, [ctypes.POINTER(BlockParams), ctypes.POINTER(Layout), _vp, _i32,
                                _vp, _vp, _vp]),
     "pma_linear": (_i32, [ctypes.POINTER(LinearArgs), _vp]),
+    "pma_rope_table": (_i32, [ctypes.POINTER(AttnParams), ctypes.POINTER(Layout), _vp, _vp]),
+    "pma_qkv_projection": (_i32, [ctypes.POINTER(AttnParams), ctypes.POINTER(Layout), _vp, _i64,
+                                  _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "pma_block_workspace_size": (_i32, [ctypes.POINTER(BlockParams), _i32,
                                         ctypes.POINTER(ctypes.c_size_t)]),
     "pma_block_forward": (_i32, [ctypes.POINTER(BlockParams), ctypes.POINTER(Layout),
@@ -252,6 +255,18 @@ def pma_qk_norm_rope(p: AttnParams, dl: DeviceLayout, q, q_ld, k, k_ld, v, v_ld,
     check(lib().pma_qk_norm_rope(ctypes.byref(p), ctypes.byref(dl.struct), ptr(q), q_ld, ptr(k),
                                  k_ld, ptr(v), v_ld, ptr(wq), ptr(wk), ptr(qh), ptr(kh), ptr(vt),
                                  stream_ptr(stream)))
+
+
+def pma_rope_table(p: AttnParams, dl: DeviceLayout, table, stream=None) -> None:
+    check(lib().pma_rope_table(ctypes.byref(p), ctypes.byref(dl.struct), ptr(table),
+                               stream_ptr(stream)))
+
+
+def pma_qkv_projection(p: AttnParams, dl: DeviceLayout, a, lda, hidden, w_qkv, wq, wk, rope,
+                       qh, kh, vt, stream=None) -> None:
+    check(lib().pma_qkv_projection(ctypes.byref(p), ctypes.byref(dl.struct), ptr(a), lda, hidden,
+                                   ptr(w_qkv), ptr(wq), ptr(wk), ptr(rope), ptr(qh), ptr(kh),
+                                   ptr(vt), stream_ptr(stream)))
 
 
 def pma_flash_attention(p: AttnParams, dl: DeviceLayout, qh, kh, vt, o, o_ld, lse=None,

@@ -127,6 +127,8 @@ pma_status api_fail(pma_status s, const char *fmt, ...) {
 }
 pma_status api_check_device() { return check_device(); }
 pma_status api_check_attn_params(const pma_attn_params *p) { return check_attn_params(p); }
+pma_status api_check_layout(const pma_layout *l) { return check_layout(l); }
+int32_t api_padded_len(int32_t L) { return padded_len(L); }
 }  // namespace pma
 
 extern "C" {

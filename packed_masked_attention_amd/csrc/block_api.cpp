@@ -2,6 +2,7 @@
 // The operations and their page citations are documented in include/pma.h.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -15,6 +16,8 @@ namespace pma {
 pma_status api_fail(pma_status s, const char *fmt, ...);
 pma_status api_check_device();
 pma_status api_check_attn_params(const pma_attn_params *p);
+pma_status api_check_layout(const pma_layout *l);
+int32_t api_padded_len(int32_t L);
 }  // namespace pma
 
 namespace {
@@ -135,19 +138,77 @@ pma_status pma_linear(const pma_linear_args *g, void *stream) {
     return PMA_OK;
 }
 
-// Workspace: a|b [L][hidden] | qkv|h [L][max(3HD, ffn)] | o [L][HD] | x1 [L][hidden]
-//            | attention operands (qh, kh, vt)
+pma_status pma_rope_table(const pma_attn_params *p, const pma_layout *layout, float *table,
+                          void *stream) {
+    pma_status st;
+    if ((st = api_check_attn_params(p)) != PMA_OK) return st;
+    if ((st = api_check_layout(layout)) != PMA_OK) return st;
+    if (!table) FAIL(PMA_ERR_NULL, "table is NULL");
+    if (!aligned(table, 8)) FAIL(PMA_ERR_ALIGN, "table must be 8-byte aligned");
+    if ((st = api_check_device()) != PMA_OK) return st;
+    PrepLaunch a;
+    memset(&a, 0, sizeof a);
+    a.L = layout->seq_len;
+    a.F = p->rope_freq_dim;
+    for (int f = 0; f < 16; ++f)
+        a.inv_freq[f] = f < a.F ? std::pow((double)p->rope_theta, -(double)f / (double)a.F) : 0.0;
+    a.pos = layout->position_ids;
+    CHECK_HIP(launch_rope_table(a, reinterpret_cast<float2 *>(table), static_cast<hipStream_t>(stream)),
+              "rope table launch");
+    return PMA_OK;
+}
+
+pma_status pma_qkv_projection(const pma_attn_params *p, const pma_layout *layout,
+                              const pma_bf16 *a_in, int64_t lda, int32_t hidden,
+                              const pma_bf16 *w_qkv, const float *q_norm_weight,
+                              const float *k_norm_weight, const float *rope_table,
+                              pma_bf16 *qh, pma_bf16 *kh, pma_bf16 *vt, void *stream) {
+    pma_status st;
+    if ((st = api_check_attn_params(p)) != PMA_OK) return st;
+    if ((st = api_check_layout(layout)) != PMA_OK) return st;
+    const int32_t H = p->num_heads, L = layout->seq_len;
+    if (H % 2 != 0) FAIL(PMA_ERR_SHAPE, "num_heads %d: the fused projection needs an even count", H);
+    if (hidden < 64 || hidden % 64 != 0) FAIL(PMA_ERR_SHAPE, "hidden %d (multiple of 64)", hidden);
+    if (!a_in || !w_qkv || !q_norm_weight || !k_norm_weight || !rope_table || !qh || !kh || !vt)
+        FAIL(PMA_ERR_NULL, "a, w_qkv, norm weights, rope table and outputs are required");
+    if (lda < hidden || lda % 8 != 0) FAIL(PMA_ERR_SHAPE, "lda %lld", (long long)lda);
+    if (!aligned(a_in, 16) || !aligned(w_qkv, 16) || !aligned(qh, 16) || !aligned(kh, 16) ||
+        !aligned(vt, 16) || !aligned(rope_table, 16) || !aligned(q_norm_weight, 16) ||
+        !aligned(k_norm_weight, 16))
+        FAIL(PMA_ERR_ALIGN, "a, w_qkv, qh, kh, vt, rope table and norm weights 16-byte aligned");
+    const int64_t HD = (int64_t)H * kHeadDim;
+    if (!fits32(L, lda) || !fits32(3 * HD, hidden)) FAIL(PMA_ERR_SHAPE, "A or W spans 2 GiB or more");
+    if ((st = api_check_device()) != PMA_OK) return st;
+    GemmLaunch g;
+    memset(&g, 0, sizeof g);
+    g.M = L; g.N = (int32_t)(3 * HD); g.K = hidden;
+    g.A = a_in; g.lda = lda;
+    g.W = w_qkv; g.ldw = hidden;
+    g.w_bytes = (uint32_t)(3 * HD * hidden * 2);
+    g.epi = p->rope_freq_dim == 16 ? kEpiQkvRope : kEpiQkvRope + 1;
+    g.Lp = api_padded_len(L); g.H = H; g.F = p->rope_freq_dim;
+    g.eps = p->qk_norm_eps;
+    g.wq = q_norm_weight; g.wk = k_norm_weight;
+    g.rope = reinterpret_cast<const float2 *>(rope_table);
+    g.qh = qh; g.kh = kh; g.vt = vt;
+    CHECK_HIP(launch_gemm(g, static_cast<hipStream_t>(stream)), "qkv projection launch");
+    return PMA_OK;
+}
+
+// Workspace: a|b [L][hidden] | x1 [L][hidden] | h [L][ffn] | o [L][HD]
+//            | attention operands (qh, kh, vt) | rope table [L][3F] float2
 pma_status pma_block_workspace_size(const pma_block_params *p, int32_t L, size_t *bytes) {
     pma_status st;
     if ((st = check_block_params(p)) != PMA_OK) return st;
     if (!bytes) FAIL(PMA_ERR_NULL, "bytes is NULL");
     if (L < 1 || L > (1 << 24)) FAIL(PMA_ERR_SHAPE, "seq_len %d", L);
     const size_t HD = (size_t)p->attn.num_heads * kHeadDim;
-    const size_t wide = HD * 3 > (size_t)p->ffn_dim ? HD * 3 : (size_t)p->ffn_dim;
+    const size_t wide = (size_t)p->ffn_dim;
     size_t attn = 0;
     if ((st = pma_attention_workspace_size(&p->attn, L, &attn)) != PMA_OK) return st;
     *bytes = round_up((size_t)L * p->hidden * 2, 256) * 2 + round_up((size_t)L * wide * 2, 256) +
-             round_up((size_t)L * HD * 2, 256) + attn;
+             round_up((size_t)L * HD * 2, 256) + attn +
+             round_up((size_t)L * 3 * p->attn.rope_freq_dim * 8, 256);
     return PMA_OK;
 }
 
@@ -171,33 +232,36 @@ pma_status pma_block_forward(const pma_block_params *p, const pma_layout *layout
 
     const int32_t hid = p->hidden, H = p->attn.num_heads, ffn = p->ffn_dim;
     const int64_t HD = (int64_t)H * kHeadDim;
-    const int64_t wide = HD * 3 > ffn ? HD * 3 : ffn;
     char *ws = static_cast<char *>(workspace);
     pma_bf16 *ab = reinterpret_cast<pma_bf16 *>(ws);                       // a, then b
     ws += round_up((size_t)L * hid * 2, 256);
     pma_bf16 *x1 = reinterpret_cast<pma_bf16 *>(ws);
     ws += round_up((size_t)L * hid * 2, 256);
-    pma_bf16 *qkvh = reinterpret_cast<pma_bf16 *>(ws);                     // qkv, then h
-    ws += round_up((size_t)L * wide * 2, 256);
+    pma_bf16 *h = reinterpret_cast<pma_bf16 *>(ws);
+    ws += round_up((size_t)L * ffn * 2, 256);
     pma_bf16 *o = reinterpret_cast<pma_bf16 *>(ws);
     ws += round_up((size_t)L * HD * 2, 256);
     void *attn_ws = ws;
-    const size_t attn_bytes = workspace_bytes - (size_t)(ws - static_cast<char *>(workspace));
+    size_t attn_bytes = 0;
+    if ((st = pma_attention_workspace_size(&p->attn, L, &attn_bytes)) != PMA_OK) return st;
+    ws += attn_bytes;
+    float *rope = reinterpret_cast<float *>(ws);
 
     // a = LN(x) (1 + scale_a) + shift_a
     if ((st = pma_ln_modulate(p, layout, table, 0, x_in, ab, stream)) != PMA_OK) return st;
-    // [Q|K|V] = a W_qkv^T
-    pma_linear_args g;
-    memset(&g, 0, sizeof g);
-    g.M = L; g.N = (int32_t)(3 * HD); g.K = hid;
-    g.A = ab; g.lda = hid; g.W = w->w_qkv; g.ldw = hid; g.C = qkvh; g.ldc = 3 * HD;
-    g.epilogue = PMA_EPI_STORE;
-    if ((st = pma_linear(&g, stream)) != PMA_OK) return st;
-    // attention path on the token-major Q, K, V columns
-    if ((st = pma_attention(&p->attn, layout, qkvh, 3 * HD, qkvh + HD, 3 * HD, qkvh + 2 * HD,
-                            3 * HD, w->q_norm_weight, w->k_norm_weight, o, HD, nullptr, attn_ws,
-                            attn_bytes, stream)) != PMA_OK)
+    // Q', K' (normed, rotated) and V^T straight from the QKV projection
+    const int32_t Lp = api_padded_len(L);
+    const size_t one = round_up((size_t)H * Lp * kHeadDim * 2, 256);
+    pma_bf16 *qh = static_cast<pma_bf16 *>(attn_ws);
+    pma_bf16 *kh = reinterpret_cast<pma_bf16 *>(static_cast<char *>(attn_ws) + one);
+    pma_bf16 *vt = reinterpret_cast<pma_bf16 *>(static_cast<char *>(attn_ws) + 2 * one);
+    if ((st = pma_rope_table(&p->attn, layout, rope, stream)) != PMA_OK) return st;
+    if ((st = pma_qkv_projection(&p->attn, layout, ab, hid, hid, w->w_qkv, w->q_norm_weight,
+                                 w->k_norm_weight, rope, qh, kh, vt, stream)) != PMA_OK)
         return st;
+    if ((st = pma_flash_attention(&p->attn, layout, qh, kh, vt, o, HD, nullptr, stream)) != PMA_OK)
+        return st;
+    pma_linear_args g;
     // x1 = x + gate_a (O W_o^T)
     memset(&g, 0, sizeof g);
     g.M = L; g.N = hid; g.K = (int32_t)HD;
@@ -211,13 +275,13 @@ pma_status pma_block_forward(const pma_block_params *p, const pma_layout *layout
     // h = silu(b W_gate^T) (b W_up^T)
     memset(&g, 0, sizeof g);
     g.M = L; g.N = ffn; g.K = hid;
-    g.A = ab; g.lda = hid; g.W = w->w_fc1; g.ldw = hid; g.C = qkvh; g.ldc = ffn;
+    g.A = ab; g.lda = hid; g.W = w->w_fc1; g.ldw = hid; g.C = h; g.ldc = ffn;
     g.epilogue = PMA_EPI_SWIGLU;
     if ((st = pma_linear(&g, stream)) != PMA_OK) return st;
     // x2 = x1 + gate_f (h W_fc2^T)
     memset(&g, 0, sizeof g);
     g.M = L; g.N = hid; g.K = ffn;
-    g.A = qkvh; g.lda = ffn; g.W = w->w_fc2; g.ldw = ffn; g.C = x_out; g.ldc = hid;
+    g.A = h; g.lda = ffn; g.W = w->w_fc2; g.ldw = ffn; g.C = x_out; g.ldc = hid;
     g.epilogue = PMA_EPI_GATE_RESIDUAL;
     g.R = x1; g.ldr = hid; g.table = table; g.num_timesteps = layout->num_timesteps;
     g.gate_chunk = 5; g.token_tags = layout->token_tags; g.timestep_indices = layout->timestep_indices;

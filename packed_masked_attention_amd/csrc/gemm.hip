@@ -8,9 +8,16 @@
 // residual written as exact bf16.
 //
 // Epilogues fused into the store:
-//   STORE          C = acc                                (QKV projection)
+//   STORE          C = acc                                (plain projection)
 //   GATE_RESIDUAL  C = R + gate[tag, ts] * acc            (O-projection, fc2)
 //   SWIGLU         C = silu(acc over gate rows) * acc over the matching up rows (fc1)
+//   QKV_ROPE       the QKV projection straight into the attention operands: the
+//                  Q and K columns are RMS-normalised per (row, head) and
+//                  rotated (3-axis RoPE) from the fp32 accumulators, written
+//                  head-major; the V columns are written transposed (V^T).
+//                  Page "MiniMax H3 Inference Engine voor Mac computers",
+//                  checkpoint layout notes: the QK normalisation and RoPE run
+//                  fused on the projection output.
 //
 // Design: 256 x 256 output tile (SWIGLU: 256 rows x 128 outputs built from
 // 128 gate rows + 128 up rows of W), K in steps of 64, eight waves (two per
@@ -50,6 +57,127 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// QKV_ROPE epilogue ids: one per rope_freq_dim F (the partner of a rotated
+// channel sits F/2 accumulator registers away in the same lane)
+constexpr int kEpiQkvF16 = kEpiQkvRope;
+constexpr int kEpiQkvF8 = kEpiQkvRope + 1;
+
+// The QKV projection's epilogue.  The 256-column tile lies inside one of Q,
+// K, V (H even) and holds two heads; wave (wm, wn) has tokens
+// m0 + 128 wm + [0, 128) and channels 64 (wn & 1) + [0, 64) of head wn / 2.
+// A lane's registers for one token: acc[i][j][v] = channel
+// 64 (wn & 1) + 32 j + 8 (v / 4) + 4 hi + v % 4 of token m0 + 128 wm + 32 i + l32.
+// Rows past the sequence have all-zero accumulators (their A rows read as
+// zero), so the padding rows up to Lp come out as zeros.
+template <int F>
+__device__ __forceinline__ void qkv_epilogue(const GemmLaunch &a, f32x16 (&acc)[4][2], int m0,
+                                             int n0, int wave, int wm, int wn, int l32, int hi,
+                                             uint16_t *as0, uint16_t *as1, uint16_t *ws0,
+                                             uint16_t *ws1) {
+    const int HD = a.H * kHeadDim;
+    const int tensor = n0 / HD;                        // 0 Q, 1 K, 2 V
+    const int head = (n0 - tensor * HD) / kHeadDim + (wn >> 1);
+    const int cb = 64 * (wn & 1);                      // the wave's first channel in the head
+    if (tensor < 2) {
+        // sum of squares per token: the lane's 32 channels, the other lane
+        // half's 32, then the paired wave's 64 through LDS
+        float *red = reinterpret_cast<float *>(as0);  // [8 waves][4][32]
+        float ss[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float t = 0.f;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) t = fmaf(acc[i][j][v], acc[i][j][v], t);
+            const uint32_t u = __float_as_uint(t);
+            const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+            ss[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+            if (hi == 0) red[(wave * 4 + i) * 32 + l32] = ss[i];
+        }
+        __syncthreads();
+        const float *w = tensor ? a.wk : a.wq;
+        uint16_t *dst = (tensor ? a.kh : a.qh) + (int64_t)head * a.Lp * kHeadDim;
+        // the lane's 32 norm weights: channels cb + 32 j + 8 g + 4 hi + [0, 4)
+        f32x4 wv[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                wv[j][g] = *reinterpret_cast<const f32x4 *>(w + cb + 32 * j + 8 * g + 4 * hi);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float tot = ss[i] + red[((wave ^ 1) * 4 + i) * 32 + l32];
+            const float rn = 1.0f / sqrtf(tot * (1.0f / kHeadDim) + a.eps);
+            const int m = m0 + 128 * wm + 32 * i + l32;
+            // rows past the sequence are zero: any in-range table row serves
+            const float2 *rope = a.rope + (int64_t)min(m, a.M - 1) * 3 * F;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                float n[16];
+#pragma unroll
+                for (int v = 0; v < 16; ++v) n[v] = acc[i][j][v] * rn * wv[j][v / 4][v % 4];
+                float y[16];
+                const int c0 = cb + 32 * j;             // first channel of this 32-channel run
+                // registers v = 4 q + e hold channel c0 + 8 q + 4 hi + e; a group
+                // of four is wholly rotated (c < 6F, four consecutive angles of
+                // one section, partner F/2 registers away) or wholly passed on
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = c0 + 8 * q + 4 * hi;
+                    if (c < 6 * F) {
+                        const int sec = c / (2 * F), f = c % F;
+                        const bool first = ((q & (F >> 3)) == 0);
+                        const f32x4 lo = *reinterpret_cast<const f32x4 *>(rope + sec * F + f);
+                        const f32x4 up = *reinterpret_cast<const f32x4 *>(rope + sec * F + f + 2);
+                        const float co[4] = {lo[0], lo[2], up[0], up[2]};
+                        const float si[4] = {lo[1], lo[3], up[1], up[3]};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int v = 4 * q + e;
+                            const float pn = n[v ^ (F / 2)];
+                            y[v] = first ? n[v] * co[e] - pn * si[e] : n[v] * co[e] + pn * si[e];
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) y[4 * q + e] = n[4 * q + e];
+                    }
+                }
+                uint16_t *drow = dst + (int64_t)m * kHeadDim + c0 + 4 * hi;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    uint2 o;
+                    o.x = pack_bf16x2(y[4 * g], y[4 * g + 1]);
+                    o.y = pack_bf16x2(y[4 * g + 2], y[4 * g + 3]);
+                    *reinterpret_cast<uint2 *>(drow + 8 * g) = o;
+                }
+            }
+        }
+    } else {
+        // V^T: each wave stages its 64 channels x 128 tokens in its own 16 KB
+        // of LDS, then writes 256-byte channel rows (tokens contiguous)
+        uint16_t *st = (wave < 2 ? as0 : wave < 4 ? as1 : wave < 6 ? ws0 : ws1) + (wave & 1) * 8192;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int cl = 32 * j + 8 * (v / 4) + 4 * hi + v % 4;
+                    st[cl * 128 + 32 * i + l32] = (uint16_t)(pack_bf16x2(acc[i][j][v], 0.f) & 0xffffu);
+                }
+        // the wave reads back only what it wrote; LDS keeps a wave's accesses in order
+        const int lane = l32 + 32 * hi;
+        uint16_t *vbase = a.vt + ((int64_t)head * kHeadDim + cb) * a.Lp + m0 + 128 * wm;
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            const int row = it * 4 + (lane >> 4), ch = lane & 15;
+            const uint4 val = *reinterpret_cast<const uint4 *>(st + row * 128 + ch * 8);
+            *reinterpret_cast<uint4 *>(vbase + (int64_t)row * a.Lp + ch * 8) = val;
+        }
+    }
+}
 
 template <int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmLaunch a) {
@@ -177,6 +305,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmLaunch a) {
 
     // ---- epilogue.  acc[i][j] register v: output row m0 + 128*wm + 32*i + l32,
     // W-tile row 64*wn + 32*j + 8*(v/4) + 4*hi + v%4.
+    if constexpr (EPI == kEpiQkvF16 || EPI == kEpiQkvF8) {
+        qkv_epilogue<EPI == kEpiQkvF16 ? 16 : 8>(a, acc, m0, n0, wave, wm, wn, l32, hi, as0, as1,
+                                                  ws0, ws1);
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int m = m0 + 128 * wm + 32 * i + l32;
@@ -248,6 +381,8 @@ hipError_t launch_gemm(const GemmLaunch &a, hipStream_t s) {
             gemm_kernel<PMA_EPI_GATE_RESIDUAL><<<grid, 512, 0, s>>>(a);
             break;
         case PMA_EPI_SWIGLU: gemm_kernel<PMA_EPI_SWIGLU><<<grid, 512, 0, s>>>(a); break;
+        case kEpiQkvF16: gemm_kernel<kEpiQkvF16><<<grid, 512, 0, s>>>(a); break;
+        case kEpiQkvF8: gemm_kernel<kEpiQkvF8><<<grid, 512, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -56,6 +56,8 @@ struct PrepLaunch {
     uint16_t *qh, *kh, *vt;
 };
 hipError_t launch_qk_norm_rope(const PrepLaunch &a, hipStream_t s);
+// (cos, sin) of every row's 3F rotation angles, built in fp64: rope[i][a*F+f]
+hipError_t launch_rope_table(const PrepLaunch &a, float2 *rope, hipStream_t s);
 
 // ----------------------------------------------------------------- flash
 struct FlashLaunch {
@@ -91,7 +93,16 @@ struct GemmLaunch {
     const float *table;
     int32_t T, gate_chunk;
     const int32_t *tags, *ts_idx;
+    // QKV projection epilogue (kEpiQkvRope): per-head RMSNorm + RoPE of the Q
+    // and K columns from the fp32 accumulators, head-major Q', K' and V^T out
+    int32_t Lp, H, F;
+    float eps;
+    const float *wq, *wk;       // norm weights [128]
+    const float2 *rope;         // (cos, sin) [L][3F]
+    uint16_t *qh, *kh, *vt;     // [H][Lp][128], [H][Lp][128], [H][128][Lp]
 };
+// internal epilogue id (beside PMA_EPI_*): the fused QKV projection
+constexpr int kEpiQkvRope = 3;
 hipError_t launch_gemm(const GemmLaunch &a, hipStream_t s);
 
 struct LnModLaunch {

@@ -168,7 +168,27 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(PrepLaunch a) {
     }
 }
 
+// One thread per (row, angle): the same fp64 angle and sincos as the table
+// above, stored as fp32 for the fused QKV projection's epilogue.
+__global__ __launch_bounds__(256) void rope_table_kernel(PrepLaunch a, float2 *rope) {
+    const int nang = 3 * a.F;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)a.L * nang) return;
+    const int row = (int)(e / nang), j = (int)(e % nang);
+    const int ax = j / a.F, f = j % a.F;
+    const double phi = (double)a.pos[3 * (int64_t)row + ax] * a.inv_freq[f];
+    double sd, cd;
+    sincos(phi, &sd, &cd);
+    rope[e] = make_float2((float)cd, (float)sd);
+}
+
 }  // namespace
+
+hipError_t launch_rope_table(const PrepLaunch &a, float2 *rope, hipStream_t s) {
+    const int64_t n = (int64_t)a.L * 3 * a.F;
+    rope_table_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a, rope);
+    return hipGetLastError();
+}
 
 hipError_t launch_qk_norm_rope(const PrepLaunch &a, hipStream_t s) {
     dim3 grid(a.Lp / kRows, (a.H + kHeads - 1) / kHeads);

@@ -155,6 +155,87 @@ def test_linear_epilogues_match_numpy(epi, M):
     assert not bad.any(), f"{int(bad.sum())} values off; worst {err.max()}"
 
 
+def _one_rounding(ref, rel=2.0 ** -16):
+    """|gpu - ref| allowed for a bf16 value rounded once from an fp32
+    computation of the fp64 reference: half an ulp of ref plus the fp32
+    computation's error.  That error is absolute on the scale of the
+    operands (an fp32 dot product's rounding does not shrink with its
+    result), so it is taken relative to |ref| + rms(ref): a few hundred
+    fp32 terms, a fp32 norm and rotation stay well below 2^-16 of it."""
+    a = np.abs(ref)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    return 2.0 ** (e - 8) + rel * (a + rms) + 1e-30
+
+
+@pytest.mark.parametrize("F,L,H,hidden", [(16, 700, 4, 512), (8, 300, 2, 256)])
+def test_qkv_projection_matches_oracle(F, L, H, hidden):
+    """pma_qkv_projection (QKV GEMM with the QK-norm + RoPE epilogue) against
+    the oracle's norm and rotation of the fp64 product, and against the
+    unfused GPU path (pma_linear + pma_qk_norm_rope) on the same inputs."""
+    import torch
+    from packed_masked_attention_amd import binding as B
+    rng = np.random.default_rng(21 + F)
+    tags = rng.integers(0, 3, L).astype(np.int32)
+    tags[rng.random(L) < 0.1] = -1
+    pos = rng.integers(0, 300, (L, 3)).astype(np.int32)
+    pos[tags == -1] = 0
+    lay = synth.layout_from_tags(tags, pos, np.zeros(L, np.int32), 1)
+    HD = H * 128
+    a_bits = synth.normal_bf16(rng, (L, hidden))
+    w_bits = synth.normal_bf16(rng, (3 * HD, hidden), 0.05)
+    wq = rng.uniform(0.5, 2.0, 128).astype(np.float32)
+    wk = rng.uniform(0.5, 2.0, 128).astype(np.float32)
+    say(f"qkv projection F={F} L={L} H={H} hidden={hidden}")
+    dl = B.pma_layout_build(lay)
+    p = B.attn_params(H, F=F)
+    Lp = B.pma_attention_padded_len(L)
+    a, w = to_dev_bf16(a_bits), to_dev_bf16(w_bits)
+    wq_d, wk_d = torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda()
+    rope = torch.empty(L, 3 * F, 2, dtype=torch.float32, device="cuda")
+    qh = torch.full((H, Lp, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kh, vt = torch.full_like(qh, float("nan")), torch.full((H, 128, Lp), float("nan"),
+                                                            dtype=torch.bfloat16, device="cuda")
+    B.pma_rope_table(p, dl, rope)
+    B.pma_qkv_projection(p, dl, a, hidden, hidden, w, wq_d, wk_d, rope, qh, kh, vt)
+    # the unfused path on the same inputs
+    qkv = torch.empty(L, 3 * HD, dtype=torch.bfloat16, device="cuda")
+    B.pma_linear(L, 3 * HD, hidden, a, hidden, w, hidden, qkv, 3 * HD, 0)
+    qh2, kh2, vt2 = torch.empty_like(qh), torch.empty_like(kh), torch.empty_like(vt)
+    B.pma_qk_norm_rope(p, dl, qkv, 3 * HD, qkv[:, HD:], 3 * HD, qkv[:, 2 * HD:], 3 * HD, wq_d, wk_d,
+                       qh2, kh2, vt2)
+    torch.cuda.synchronize()
+
+    # rope table: fp32 rounding of the fp64 cos/sin of pos[i][a] * theta^(-f/F)
+    inv = oracle.inv_freq(F, 10000.0)
+    phi = pos[:, :, None].astype(np.float64) * inv[None, None, :]       # [L, 3, F]
+    tab = rope.cpu().numpy().reshape(L, 3, F, 2)
+    assert np.abs(tab[..., 0] - np.cos(phi)).max() <= 2.0 ** -24
+    assert np.abs(tab[..., 1] - np.sin(phi)).max() <= 2.0 ** -24
+
+    A64, W64 = oracle.bf16_to_f64(a_bits), oracle.bf16_to_f64(w_bits)
+    q, k, v = (A64 @ W64[i * HD:(i + 1) * HD].T for i in range(3))
+    for name, got_t, x, wv in (("q'", qh, q, wq), ("k'", kh, k, wk)):
+        ref = oracle.qk_norm_rope(x, H, 128, wv.astype(np.float64), pos, F=F).transpose(1, 0, 2)
+        got = bf16_to_np(got_t)
+        err = np.abs(got[:, :L] - ref)
+        bad = err > _one_rounding(ref)
+        say(f"  {name}: max err {err.max():.3e}, {int(bad.sum())} over one rounding")
+        assert not bad.any()
+        assert np.all(got[:, L:] == 0), f"{name} padding rows"
+    vref = v.reshape(L, H, 128).transpose(1, 2, 0)
+    vg = bf16_to_np(vt)
+    assert not (np.abs(vg[:, :, :L] - vref) > _one_rounding(vref)).any(), "v^T"
+    assert np.all(vg[:, :, L:] == 0), "v^T padding columns"
+    # V^T is the same bf16 product both ways; Q', K' differ only by the
+    # unfused path's extra rounding of Q and K before the norm
+    assert torch.equal(vt.view(torch.int16), vt2.view(torch.int16))
+    for got_t, ref_t in ((qh, qh2), (kh, kh2)):
+        g, r2 = bf16_to_np(got_t), bf16_to_np(ref_t)
+        rel = np.abs(g - r2).max() / np.abs(r2).max()
+        assert rel < 2.0 ** -6, rel
+
+
 def test_block_small_matches_oracle():
     inp = _small_inputs(seed=5)
     say("block small: L=300 hidden=256 H=2 ffn=512, 20 padding rows, T=2")
@@ -162,7 +243,8 @@ def test_block_small_matches_oracle():
     r.adaln()
     got = r.forward()
     mod = r.table.cpu().numpy().astype(np.float64)   # same table on both sides
-    ref = oblock.block_forward(inp, mod=mod)
+    # an even head count takes the fused QKV projection (Q, K not stored)
+    ref = oblock.block_forward(inp, mod=mod, fused_qkv=inp["heads"] % 2 == 0)
     _block_close(got, ref, "block small")
 
 
@@ -193,7 +275,7 @@ def test_block_full_size_sampled_rows():
     mod = r.table.cpu().numpy().astype(np.float64)
     ref_mod = oblock.adaln_table(inp["temb"], inp["w_ada"])
     assert np.allclose(mod, ref_mod, rtol=1e-4, atol=1e-4 * np.abs(ref_mod).max())
-    ref = oblock.block_forward(inp, rows=rows, mod=mod)
+    ref = oblock.block_forward(inp, rows=rows, mod=mod, fused_qkv=True)
     _block_close(got[rows], ref, "block L8192 sampled rows")
 
 

@@ -412,6 +412,25 @@ def test_block_matches_torch_composition():
                        rtol=1e-10, atol=1e-10)
 
 
+def test_block_fused_qkv_only_moves_rounding():
+    """The fused-projection option drops the bf16 storage of Q and K: in fp64
+    mode it is the same composition (pinned to torch above); in storage mode
+    its intermediate Q' differs from the unfused one by at most one rounding of
+    the pre-norm Q, and V is untouched."""
+    inp = _tiny_block(seed=14)
+    a64 = oblock.block_forward(inp, store_bf16=False)
+    f64 = oblock.block_forward(inp, store_bf16=False, fused_qkv=True)
+    assert np.array_equal(a64, f64)
+    _, ia = oblock.block_forward(inp, return_intermediates=True)
+    _, ib = oblock.block_forward(inp, return_intermediates=True, fused_qkv=True)
+    HD = inp["heads"] * inp["head_dim"]
+    assert np.array_equal(ia["kv"][:, HD:], ib["kv"][:, HD:])          # V still stored bf16
+    assert not np.array_equal(ia["kv"][:, :HD], ib["kv"][:, :HD])      # K no longer rounded
+    assert np.array_equal(oracle.bf16_storage(ib["kv"][:, :HD]), ia["kv"][:, :HD])
+    rel = np.abs(ia["qn"] - ib["qn"]).max() / np.abs(ib["qn"]).max()
+    assert 0 < rel < 2.0 ** -6
+
+
 def test_block_zero_gates_is_identity():
     inp = _tiny_block(seed=12)
     hid = inp["hidden"]
