@@ -50,30 +50,32 @@ def source_hash(path: str) -> str:
 
 
 def gpu_state():
-    """Clocks and power of GPU 0 from rocm-smi (a child process), or None when
-    it is unavailable.  Read outside the timed region."""
+    """Current sclk/mclk DPM levels and average power of the first amdgpu card,
+    read from sysfs (no child process: the GPU is initialised by then), or
+    None where unavailable.  Read outside the timed region."""
+    import glob
     import re
-    import subprocess
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
-                           capture_output=True, text=True, timeout=30)
-        d = json.loads(r.stdout)
-    except Exception:
-        return None
-    card = next((v for k, v in d.items() if k.startswith("card")), None)
-    if not isinstance(card, dict):
-        return None
     out = {}
-    for key, val in card.items():
-        k, v = key.lower(), str(val)
-        mhz = re.search(r"([0-9.]+)\s*mhz", v, re.IGNORECASE)
-        if mhz and "sclk" in k:
-            out["sclk_mhz"] = float(mhz.group(1))
-        elif mhz and "mclk" in k:
-            out["mclk_mhz"] = float(mhz.group(1))
-        elif "power" in k and "(w)" in k and re.fullmatch(r"\s*[0-9.]+\s*", v):
-            out["power_w"] = float(v)
-    return out or None
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for key, name in (("sclk_mhz", "pp_dpm_sclk"), ("mclk_mhz", "pp_dpm_mclk")):
+            try:
+                with open(os.path.join(dev, name)) as fh:
+                    for line in fh:
+                        m = re.search(r"([0-9]+)\s*mhz\s*\*", line, re.IGNORECASE)
+                        if m:
+                            out[key] = float(m.group(1))
+            except OSError:
+                pass
+        for f in glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_average")) + \
+                glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_input")):
+            try:
+                with open(f) as fh:
+                    out.setdefault("power_w", int(fh.read().strip()) / 1e6)
+            except (OSError, ValueError):
+                pass
+        if out:
+            return out
+    return None
 
 
 def attention_flops(tags, H: int, D: int) -> int:
