@@ -207,6 +207,56 @@ def make_block_inputs(L: int, hidden: int, heads: int, head_dim: int, ffn: int,
             "heads": heads, "head_dim": head_dim, "ffn": ffn, "temb_dim": temb_dim}
 
 
+def normal_f32(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
+    return (rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std)).astype(np.float32)
+
+
+def make_io_inputs(layout: dict, hidden: int = 5376, video_channels: int = 96,
+                   audio_channels: int = 32, video_out: int = 96, audio_out: int = 32,
+                   freq_dim: int = 256, inner_dim: int = 5376, temb_dim: int = 2688,
+                   seed: int = 5, timesteps=None) -> dict:
+    """Inputs of the steps either side of the block stack.
+
+    Draw order (fp32 unless noted): timesteps ~ U[0, 1) [T] (unless given),
+    w1 [inner, freq] ~ N(0, 1/freq), b1 [inner] ~ N(0, 0.02^2),
+    w2 [temb, inner] ~ N(0, 1/inner), b2 [temb] ~ N(0, 0.02^2),
+    video rows [num_video, video_channels] ~ N(0, 1),
+    w_video [hidden, video_channels] ~ N(0, 1/video_channels), b_video ~ N(0, 0.02^2),
+    audio rows / w_audio / b_audio likewise, text rows bf16 [num_text, hidden] ~ N(0, 1),
+    w_mod [2, 2*hidden, temb] ~ N(0, 0.02^2), w_vout [video_out, hidden] ~ N(0, 1/hidden),
+    b_vout ~ N(0, 0.02^2), w_aout / b_aout likewise, x bf16 [L, hidden] ~ N(0, 1).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T = int(layout["T"])
+    nv, na, nt = (int(np.asarray(layout[k]).size) for k in ("video_idx", "audio_idx", "text_idx"))
+    if timesteps is None:
+        t = rng.random(T, dtype=np.float32)
+    else:
+        t = np.asarray(timesteps, dtype=np.float32).reshape(T)
+    out = {"t": t}
+    out["w1"] = normal_f32(rng, (inner_dim, freq_dim), freq_dim ** -0.5)
+    out["b1"] = normal_f32(rng, (inner_dim,), 0.02)
+    out["w2"] = normal_f32(rng, (temb_dim, inner_dim), inner_dim ** -0.5)
+    out["b2"] = normal_f32(rng, (temb_dim,), 0.02)
+    out["video"] = normal_f32(rng, (nv, video_channels))
+    out["w_video"] = normal_f32(rng, (hidden, video_channels), video_channels ** -0.5)
+    out["b_video"] = normal_f32(rng, (hidden,), 0.02)
+    out["audio"] = normal_f32(rng, (na, audio_channels))
+    out["w_audio"] = normal_f32(rng, (hidden, audio_channels), audio_channels ** -0.5)
+    out["b_audio"] = normal_f32(rng, (hidden,), 0.02)
+    out["text"] = normal_bf16(rng, (nt, hidden))
+    out["w_mod"] = normal_f32(rng, (2, 2 * hidden, temb_dim), 0.02)
+    out["w_vout"] = normal_f32(rng, (video_out, hidden), hidden ** -0.5)
+    out["b_vout"] = normal_f32(rng, (video_out,), 0.02)
+    out["w_aout"] = normal_f32(rng, (audio_out, hidden), hidden ** -0.5)
+    out["b_aout"] = normal_f32(rng, (audio_out,), 0.02)
+    out["x"] = normal_bf16(rng, (int(layout["L"]), hidden))
+    out.update(layout=layout, hidden=hidden, video_channels=video_channels,
+               audio_channels=audio_channels, video_out=video_out, audio_out=audio_out,
+               freq_dim=freq_dim, inner_dim=inner_dim, temb_dim=temb_dim)
+    return out
+
+
 def make_block_workload(wl: Workload) -> dict:
     return make_block_inputs(wl.L, wl.hidden, wl.H, wl.D, wl.ffn, wl.temb_dim, wl.T,
                              wl.seed, wl.weight_std, text=wl.text, video=wl.video,
