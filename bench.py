@@ -19,6 +19,11 @@ L=8192, hidden 5376, ffn 14336; value is the block's algorithmic TFLOP/s and
 the roofline object is the fc1+SwiGLU GEMM (the block's largest kernel) timed
 in its own launches.
 
+With --workload io_L8192 (or io_L16384) the step is the input/output path on
+that packed layout: timestep MLP, output-head table, patch projections into
+the packed stream, output heads; value is its fp32 TFLOP/s and the roofline
+object is the video patch projection against the fp32 MFMA peak.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--copy-probe BYTES]
 """
@@ -224,6 +229,106 @@ def block_bench(args) -> int:
     return 0
 
 
+FP32_PEAK_TFLOPS = 157.3          # dense fp32 MFMA
+
+
+def io_bench(args) -> int:
+    """The steps either side of the block stack on one packed layout: timestep
+    MLP (T distinct timesteps), output-head modulation table, input
+    projections + text scatter into the packed stream, and the two output
+    heads.  value = fp32 TFLOP/s of the whole step; roofline = the video
+    patch projection (the largest single-launch contraction), fp32 MFMA."""
+    import numpy as np
+    import torch
+    from packed_masked_attention_amd import binding as B
+    from packed_masked_attention_amd import synth
+
+    torch.cuda.set_device(0)
+    base = {"io_L8192": "block_L8192", "io_L16384": "masked_L16384"}.get(args.workload)
+    if base is None:
+        log(f"unknown workload {args.workload}")
+        return 2
+    lay = synth.make_layout(synth.workload(base))
+    hidden, fd, inner, E = 5376, 256, 5376, 2688
+    log(f"[bench] generating {args.workload} inputs")
+    d = synth.make_io_inputs(lay, hidden=hidden, freq_dim=fd, inner_dim=inner, temb_dim=E)
+    dev = torch.device("cuda", 0)
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    T = lay["T"]
+    nv, na, nt = (int(lay[k].size) for k in ("video_idx", "audio_idx", "text_idx"))
+    tp, p = B.temb_params(fd, inner, E), B.io_params(hidden, time_embed_dim=E)
+    t, w1, b1, w2, b2 = (f(d[k]) for k in ("t", "w1", "b1", "w2", "b2"))
+    inner_t = torch.empty(T, inner, device=dev)
+    temb = torch.empty(T, E, device=dev)
+    temb_b = torch.empty(T, E, dtype=torch.bfloat16, device=dev)
+    w_mod = f(d["w_mod"])
+    table = torch.empty(2, T, 2, hidden, device=dev)
+    dl = B.pma_layout_build(lay, device=dev)
+    x = torch.empty(lay["L"], hidden, dtype=torch.bfloat16, device=dev).normal_()
+    video, wv, bv = f(d["video"]), f(d["w_video"]), f(d["b_video"])
+    audio, wa, ba = f(d["audio"]), f(d["w_audio"]), f(d["b_audio"])
+    text = torch.from_numpy(d["text"].view(np.int16)).to(dev).view(torch.bfloat16)
+    hw = [f(d[k]) for k in ("w_vout", "b_vout", "w_aout", "b_aout")]
+    vout = torch.empty(nv, 96, device=dev)
+    aout = torch.empty(na, 32, device=dev)
+    ws = torch.empty(B.pma_unpack_workspace_size(p, nv, na), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.pma_timestep_embed(tp, T, t, w1, b1, w2, b2, inner_t, temb, temb_b)
+        B.pma_head_table(p, T, temb, w_mod, table)
+        B.pma_pack_rows(p, dl, video, wv, bv, audio, wa, ba, text, hidden, x)
+        B.pma_unpack_rows(p, dl, x, table, *hw, vout, aout, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    rows_f = nv * 96 + na * 32
+    flops = (2 * T * (fd * inner + inner * E) + 2 * T * E * 4 * hidden
+             + 2 * rows_f * hidden * 2)
+    # the video projection alone: a descriptor naming only the video rows
+    desc_v = B.LayoutDesc(lay["L"], T, dl.desc.token_tags, dl.desc.position_ids,
+                          dl.desc.timestep_indices, dl.desc.video_indices, None, None, nv, 0, 0)
+    dlv = B.DeviceLayout(dl.arrays, dl.workspace, dl.struct, desc_v)
+    for _ in range(3):
+        B.pma_pack_rows(p, dlv, video, wv, bv, None, None, None, None, hidden, x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        B.pma_pack_rows(p, dlv, video, wv, bv, None, None, None, None, hidden, x)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    proj_ms = e0.elapsed_time(e1) / args.steps
+    proj_flops = 2 * nv * 96 * hidden
+    achieved = proj_flops / (proj_ms * 1e-3) / 1e12
+    value = flops / (ms_step * 1e-3) / 1e12
+    outj = {
+        "metric": "input/output path fp32 TFLOP/s (timestep MLP, head table, patch projections, "
+                  "output heads)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "seq_len": int(lay["L"]), "hidden": hidden,
+                   "rows": {"video": nv, "audio": na, "text": nt}, "num_timesteps": T,
+                   "freq_dim": fd, "time_embed_hidden_dim": inner, "time_embed_dim": E,
+                   "algorithmic_flops": flops,
+                   "step": "timestep MLP + head table + pack (projections, text scatter) + "
+                           "unpack (output heads)"},
+        "roofline": {"kernel": "proj_scatter_kernel (video patch projection)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": FP32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 4),
+                     "traffic": None, "avg_ms": round(proj_ms, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(outj), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,6 +350,8 @@ def main() -> int:
         return 0
     if args.workload.startswith("block"):
         return block_bench(args)
+    if args.workload.startswith("io_"):
+        return io_bench(args)
 
     import numpy as np
     import torch

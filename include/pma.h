@@ -336,6 +336,103 @@ pma_status pma_block_forward(const pma_block_params *p, const pma_layout *layout
                              const pma_bf16 *x_in, pma_bf16 *x_out, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/* ======================================================================
+ * 4. Input and output path: timestep MLP, row pack, output heads
+ * ----------------------------------------------------------------------
+ * [H3] constructor parameters: freq_dim (256) of the sinusoidal timestep
+ * embedding, timesteps taken unscaled in [0, 1]; time_embed_hidden_dim
+ * (5376) and time_embed_dim (2688), the timestep MLP's inner and output
+ * widths; in_channels * prod(patch_size) (24 * 4 = 96) and audio_in_channels
+ * (32), the widths of the latent rows; final_norm_eps (1e-5) of norm_out.
+ * [H3] forward parameters: the video, audio and text rows arrive ordered as
+ * video_indices, audio_indices and text_indices; timestep holds the distinct
+ * values and timestep_indices points each row into it.  [H3] returns: the
+ * video and audio velocities in the row order of their index tensors.  [H3]
+ * intro: the patch projections, the timestep MLP and the two output heads
+ * are fp32.  [ENG] "Exacte DiT fusions": the fp32 patch projections round
+ * straight to bf16 into the packed hidden stream; the final audio/video
+ * AdaLN reads its rows at their offsets in the residual stream and the
+ * heads modulate while loading their projection tiles.
+ *
+ * Readings of the pages' open points:
+ *   e(t) = [cos(t w_j) | sin(t w_j)], w_j = max_period^(-j / half),
+ *     half = freq_dim / 2, j = 0..half-1, max_period 10000;
+ *   temb = W2 silu(W1 e + b1) + b2                (fp32)
+ *   x[idx[i]] = bf16(rows[i] W^T + b)             video and audio rows
+ *   x[text_idx[i]] = text[i]                      projected text rows (bf16)
+ *   head m (0 video, 1 audio): (shift, scale) = temb[ts] W_mod[m]^T, no bias,
+ *     out[i] = (LN(x[idx[i]]) * (1 + scale) + shift) W_out^T + b_out (fp32),
+ *     LN without affine, population variance, eps = final_norm_eps, ts the
+ *     row's timestep index.
+ * Weights are fp32 [out][in].
+ * ====================================================================== */
+
+typedef struct {
+    int32_t freq_dim;      /* sinusoid width: multiple of 4, 4..2048        */
+    int32_t inner_dim;     /* time_embed_hidden_dim: multiple of 4          */
+    int32_t embed_dim;     /* time_embed_dim E: multiple of 4                 */
+    float max_period;      /* > 1 (10000)                                     */
+} pma_temb_params;
+
+/* Timestep MLP for T <= 8 distinct timesteps.  timestep: fp32 [T];
+ * w1 [inner][freq_dim], b1 [inner], w2 [E][inner], b2 [E] fp32;
+ * inner: fp32 [T][inner] (written; the MLP's hidden activation);
+ * temb: fp32 [T][E]; temb_bf16 (optional, may be NULL): the same values
+ * rounded to bf16, the input pma_adaln_table takes.  Weights and activations
+ * 16-byte aligned. */
+pma_status pma_timestep_embed(const pma_temb_params *p, int32_t num_timesteps,
+                              const float *timestep, const float *w1, const float *b1,
+                              const float *w2, const float *b2, float *inner, float *temb,
+                              pma_bf16 *temb_bf16, void *stream);
+
+typedef struct {
+    int32_t hidden;          /* packed stream width: multiple of 128, <= 8192   */
+    int32_t video_channels;  /* video row width: multiple of 32 (96)            */
+    int32_t audio_channels;  /* audio row width: multiple of 32 (32)            */
+    int32_t video_out;       /* video head width: multiple of 32, <= 128 (96)   */
+    int32_t audio_out;       /* audio head width: multiple of 32, <= 128 (32)   */
+    int32_t time_embed_dim;  /* E: multiple of 4                                */
+    float final_norm_eps;    /* >= 0 (1e-5)                                     */
+} pma_io_params;
+
+/* Write the input rows into the packed stream x (bf16 [seq_len][hidden]):
+ * video_rows fp32 [num_video][video_channels] through w_video
+ * [hidden][video_channels] + b_video, audio_rows likewise, and the projected
+ * text rows (bf16, row stride text_ld >= hidden) copied.  desc supplies
+ * seq_len and the device index arrays (counts may be 0, pointers then
+ * ignored).  Rows named by no index are not written; index entries outside
+ * [0, seq_len) are skipped (pma_layout_build flags them).  Indices must be
+ * distinct.  fp32 arrays and x 16-byte aligned; text_ld % 8 == 0. */
+pma_status pma_pack_rows(const pma_io_params *p, const pma_layout_desc *desc,
+                         const float *video_rows, const float *w_video, const float *b_video,
+                         const float *audio_rows, const float *w_audio, const float *b_audio,
+                         const pma_bf16 *text_rows, int64_t text_ld, pma_bf16 *x,
+                         void *stream);
+
+/* Output-head modulation table: table[m][t][k][c] = sum_e temb[t][e] *
+ * w_mod[m][k*hidden + c][e], k = 0 shift, 1 scale.  temb fp32 [T][E];
+ * w_mod fp32 [2][2*hidden][E]; table fp32 [2][T][2][hidden].  T <= 8. */
+pma_status pma_head_table(const pma_io_params *p, int32_t num_timesteps, const float *temb,
+                          const float *w_mod, float *table, void *stream);
+
+/* Device workspace of pma_unpack_rows for the given row counts. */
+pma_status pma_unpack_workspace_size(const pma_io_params *p, int32_t num_video,
+                                     int32_t num_audio, size_t *bytes);
+
+/* Output heads: video_out fp32 [num_video][video_out] and audio_out fp32
+ * [num_audio][audio_out] from the rows of x (bf16 [seq_len][hidden]) named by
+ * desc's video and audio indices, in index order.  table from
+ * pma_head_table with T = desc->num_timesteps (<= 8); w_video_out
+ * [video_out][hidden], w_audio_out [audio_out][hidden] and the biases fp32.
+ * A row whose timestep index is outside [0, T) is not modulated; an index
+ * entry outside [0, seq_len) yields a row equal to the bias.  All arrays
+ * 16-byte aligned; workspace >= pma_unpack_workspace_size, 256-byte aligned. */
+pma_status pma_unpack_rows(const pma_io_params *p, const pma_layout_desc *desc,
+                           const pma_bf16 *x, const float *table, const float *w_video_out,
+                           const float *b_video_out, const float *w_audio_out,
+                           const float *b_audio_out, float *video_out, float *audio_out,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

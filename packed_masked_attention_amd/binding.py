@@ -73,6 +73,17 @@ class LinearArgs(ctypes.Structure):
 
 EPI_STORE, EPI_GATE_RESIDUAL, EPI_SWIGLU = 0, 1, 2
 
+
+class TembParams(ctypes.Structure):
+    _fields_ = [("freq_dim", _i32), ("inner_dim", _i32), ("embed_dim", _i32),
+                ("max_period", ctypes.c_float)]
+
+
+class IoParams(ctypes.Structure):
+    _fields_ = [("hidden", _i32), ("video_channels", _i32), ("audio_channels", _i32),
+                ("video_out", _i32), ("audio_out", _i32), ("time_embed_dim", _i32),
+                ("final_norm_eps", ctypes.c_float)]
+
 _SIGS = {
     "pma_status_string": (ctypes.c_char_p, [_i32]),
     "pma_last_error": (ctypes.c_char_p, []),
@@ -105,6 +116,15 @@ _SIGS = {
     "pma_block_forward": (_i32, [ctypes.POINTER(BlockParams), ctypes.POINTER(Layout),
                                  ctypes.POINTER(BlockWeights), _vp, _vp, _vp, _vp,
                                  ctypes.c_size_t, _vp]),
+    "pma_timestep_embed": (_i32, [ctypes.POINTER(TembParams), _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _vp, _vp]),
+    "pma_pack_rows": (_i32, [ctypes.POINTER(IoParams), ctypes.POINTER(LayoutDesc), _vp, _vp, _vp,
+                             _vp, _vp, _vp, _vp, _i64, _vp, _vp]),
+    "pma_head_table": (_i32, [ctypes.POINTER(IoParams), _i32, _vp, _vp, _vp, _vp]),
+    "pma_unpack_workspace_size": (_i32, [ctypes.POINTER(IoParams), _i32, _i32,
+                                         ctypes.POINTER(ctypes.c_size_t)]),
+    "pma_unpack_rows": (_i32, [ctypes.POINTER(IoParams), ctypes.POINTER(LayoutDesc), _vp, _vp,
+                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
 }
 
 _lib = None
@@ -332,3 +352,56 @@ def pma_block_forward(p: BlockParams, dl: DeviceLayout, w: BlockWeights, table, 
     check(lib().pma_block_forward(ctypes.byref(p), ctypes.byref(dl.struct), ctypes.byref(w),
                                   ptr(table), ptr(x_in), ptr(x_out), ptr(workspace),
                                   workspace.numel(), stream_ptr(stream)))
+
+
+# ------------------------------------------------------- input / output path
+
+def temb_params(freq_dim: int = 256, inner_dim: int = 5376, embed_dim: int = 2688,
+                max_period: float = 10000.0) -> TembParams:
+    return TembParams(freq_dim, inner_dim, embed_dim, max_period)
+
+
+def io_params(hidden: int = 5376, video_channels: int = 96, audio_channels: int = 32,
+              video_out: int = 96, audio_out: int = 32, time_embed_dim: int = 2688,
+              final_norm_eps: float = 1e-5) -> IoParams:
+    return IoParams(hidden, video_channels, audio_channels, video_out, audio_out, time_embed_dim,
+                    final_norm_eps)
+
+
+def pma_timestep_embed(p: TembParams, num_timesteps: int, timestep, w1, b1, w2, b2, inner, temb,
+                       temb_bf16=None, stream=None) -> None:
+    check(lib().pma_timestep_embed(ctypes.byref(p), num_timesteps, ptr(timestep), ptr(w1),
+                                   ptr(b1), ptr(w2), ptr(b2), ptr(inner), ptr(temb),
+                                   ptr(temb_bf16), stream_ptr(stream)))
+
+
+def pma_pack_rows(p: IoParams, dl: DeviceLayout, video, w_video, b_video, audio, w_audio,
+                  b_audio, text, text_ld, x, stream=None) -> None:
+    check(lib().pma_pack_rows(ctypes.byref(p), ctypes.byref(dl.desc), ptr(video), ptr(w_video),
+                              ptr(b_video), ptr(audio), ptr(w_audio), ptr(b_audio), ptr(text),
+                              text_ld, ptr(x), stream_ptr(stream)))
+
+
+def pma_head_table(p: IoParams, num_timesteps: int, temb, w_mod, table, stream=None) -> None:
+    check(lib().pma_head_table(ctypes.byref(p), num_timesteps, ptr(temb), ptr(w_mod), ptr(table),
+                               stream_ptr(stream)))
+
+
+def pma_unpack_workspace_size(p: IoParams, num_video: int, num_audio: int) -> int:
+    n = ctypes.c_size_t()
+    check(lib().pma_unpack_workspace_size(ctypes.byref(p), num_video, num_audio, ctypes.byref(n)))
+    return n.value
+
+
+def pma_unpack_rows(p: IoParams, dl: DeviceLayout, x, table, w_video_out, b_video_out,
+                    w_audio_out, b_audio_out, video_out, audio_out, workspace=None,
+                    stream=None) -> None:
+    import torch
+    d = dl.desc
+    nbytes = pma_unpack_workspace_size(p, d.num_video, d.num_audio)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    check(lib().pma_unpack_rows(ctypes.byref(p), ctypes.byref(d), ptr(x), ptr(table),
+                                ptr(w_video_out), ptr(b_video_out), ptr(w_audio_out),
+                                ptr(b_audio_out), ptr(video_out), ptr(audio_out), ptr(workspace),
+                                workspace.numel(), stream_ptr(stream)))

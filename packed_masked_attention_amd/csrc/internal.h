@@ -124,4 +124,59 @@ struct AdaLnLaunch {
 hipError_t launch_adaln_table(const AdaLnLaunch &a, hipStream_t s);
 int adaln_max_t();
 
+// ------------------------------------------------------- input / output path
+struct GemvLaunch {
+    int32_t T, K, N;
+    int32_t group_rows;        // out[(g*T + t)*group_rows + n % group_rows], g = n / group_rows
+    const float *x;            // [T][K] (unused when timestep is set)
+    const float *timestep;     // [T]: x = sinusoid of these (K = freq_dim)
+    double log_max_period;
+    const float *W;            // [N][K]
+    const float *b;            // [N] or null
+    int32_t silu;
+    float *out;
+    uint16_t *out_bf16;        // optional bf16 copy, same layout
+};
+hipError_t launch_gemv(const GemvLaunch &a, hipStream_t s);
+int gemv_max_t();
+
+struct ProjLaunch {
+    int32_t rows, K, N, L;     // N % 128 == 0, K % 32 == 0
+    const float *X;            // [rows][K]
+    const float *W;            // [N][K]
+    const float *b;            // [N]
+    const int32_t *idx;        // [rows] destination rows
+    uint16_t *out;
+    int64_t ld_out;
+};
+hipError_t launch_proj_scatter(const ProjLaunch &a, hipStream_t s);
+
+struct TextScatterLaunch {
+    int32_t rows, hidden, L;
+    const uint16_t *src;
+    int64_t ld_src;
+    const int32_t *idx;
+    uint16_t *out;
+    int64_t ld_out;
+};
+hipError_t launch_text_scatter(const TextScatterLaunch &a, hipStream_t s);
+
+struct HeadLaunch {
+    int32_t rows, hidden, nout, L, T, head, splits;
+    float eps;
+    const uint16_t *x;
+    int64_t ld_x;
+    const int32_t *idx, *ts_idx;
+    const float *table;        // [2][T][2][hidden]
+    const float *W, *b;        // [nout][hidden], [nout]
+    float2 *stats;             // [rows]
+    float *partial;            // [splits][rows][nout]
+    float *out;                // [rows][nout]
+};
+hipError_t launch_head(const HeadLaunch &a, hipStream_t s);
+int head_max_hidden();
+int head_max_out();
+int head_max_t();     // distinct timesteps the head kernels accept
+int head_k_chunk();   // each head K range is a multiple of this
+
 }  // namespace pma

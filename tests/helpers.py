@@ -119,3 +119,16 @@ class AttentionRun:
 
     def lse_np(self) -> np.ndarray:
         return self.lse.cpu().numpy().T  # [L, H]
+
+
+def one_rounding(ref, rel=2.0 ** -16):
+    """|gpu - ref| allowed for a bf16 value rounded once from an fp32
+    computation of the fp64 reference: half an ulp of ref plus the fp32
+    computation's error.  That error is absolute on the scale of the
+    operands (an fp32 dot product's rounding does not shrink with its
+    result), so it is taken relative to |ref| + rms(ref): a few hundred
+    fp32 terms, a fp32 norm and rotation stay well below 2^-16 of it."""
+    a = np.abs(ref)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    return 2.0 ** (e - 8) + rel * (a + rms) + 1e-30

@@ -79,3 +79,46 @@ def test_host_side_argument_errors(lib):
     assert lib.pma_flash_attention(ctypes.byref(p), ctypes.byref(big), fake, fake, fake, fake,
                                    56 * 128, None, None) == 2
     assert "k-tiles" in lib.pma_last_error().decode()
+
+
+def test_io_path_host_side_argument_errors(lib):
+    n = ctypes.c_size_t()
+    fake = ctypes.c_void_p(256)
+    p = B.io_params()
+    assert lib.pma_unpack_workspace_size(ctypes.byref(p), 7200, 480, ctypes.byref(n)) == 0
+    # stats (8 B per row) and the K-range partials of every output, each part
+    # 256-byte aligned; 7200 rows use 12 ranges of 448 columns, 480 rows 84 of 64
+    want = sum((s + 255) // 256 * 256 for s in (8 * 7200, 4 * 12 * 7200 * 96, 8 * 480,
+                                                 4 * 84 * 480 * 32))
+    assert n.value == want
+    for bad in (B.io_params(hidden=100), B.io_params(video_channels=48), B.io_params(audio_out=160),
+                B.io_params(time_embed_dim=6), B.io_params(final_norm_eps=-1.0)):
+        assert lib.pma_unpack_workspace_size(ctypes.byref(bad), 1, 1, ctypes.byref(n)) == 2
+    d = B.LayoutDesc(100, 1, fake, fake, fake, fake, None, None, 10, 0, 0)
+    # workspace too small, then misaligned
+    assert lib.pma_unpack_rows(ctypes.byref(p), ctypes.byref(d), fake, fake, fake, fake, fake,
+                               fake, fake, fake, fake, 16, None) == 4
+    assert lib.pma_unpack_rows(ctypes.byref(p), ctypes.byref(d), fake, fake, fake, fake, fake,
+                               fake, fake, fake, ctypes.c_void_p(264), 1 << 24, None) == 3
+    d9 = B.LayoutDesc(100, 9, fake, fake, fake, fake, None, None, 10, 0, 0)
+    assert lib.pma_unpack_rows(ctypes.byref(p), ctypes.byref(d9), fake, fake, fake, fake, fake,
+                               fake, fake, fake, fake, 1 << 24, None) == 2
+    # counts beyond seq_len; an index array missing for a non-zero count
+    d2 = B.LayoutDesc(100, 1, fake, fake, fake, fake, fake, fake, 60, 30, 20)
+    assert lib.pma_pack_rows(ctypes.byref(p), ctypes.byref(d2), fake, fake, fake, fake, fake, fake,
+                             fake, 5376, fake, None) == 2
+    d3 = B.LayoutDesc(100, 1, fake, fake, fake, None, fake, fake, 10, 0, 0)
+    assert lib.pma_pack_rows(ctypes.byref(p), ctypes.byref(d3), fake, fake, fake, fake, fake, fake,
+                             fake, 5376, fake, None) == 1
+    d4 = B.LayoutDesc(100, 1, fake, fake, fake, fake, fake, fake, 10, 0, 5)
+    assert lib.pma_pack_rows(ctypes.byref(p), ctypes.byref(d4), fake, fake, fake, fake, fake, fake,
+                             fake, 5370, fake, None) == 2
+    assert "text_ld" in lib.pma_last_error().decode()
+    tp = B.temb_params()
+    assert lib.pma_timestep_embed(ctypes.byref(tp), 9, fake, fake, fake, fake, fake, fake, fake,
+                                  None, None) == 2
+    tp_bad = B.temb_params(freq_dim=254)
+    assert lib.pma_timestep_embed(ctypes.byref(tp_bad), 1, fake, fake, fake, fake, fake, fake,
+                                  fake, None, None) == 2
+    assert lib.pma_head_table(ctypes.byref(p), 0, fake, fake, fake, None) == 2
+    assert lib.pma_head_table(ctypes.byref(p), 1, ctypes.c_void_p(260), fake, fake, None) == 3

@@ -18,7 +18,7 @@ import pytest
 import oracle
 from oracle import block as oblock
 from packed_masked_attention_amd import synth
-from tests.helpers import bf16_to_np, say, to_dev_bf16
+from tests.helpers import bf16_to_np, one_rounding, say, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -155,17 +155,7 @@ def test_linear_epilogues_match_numpy(epi, M):
     assert not bad.any(), f"{int(bad.sum())} values off; worst {err.max()}"
 
 
-def _one_rounding(ref, rel=2.0 ** -16):
-    """|gpu - ref| allowed for a bf16 value rounded once from an fp32
-    computation of the fp64 reference: half an ulp of ref plus the fp32
-    computation's error.  That error is absolute on the scale of the
-    operands (an fp32 dot product's rounding does not shrink with its
-    result), so it is taken relative to |ref| + rms(ref): a few hundred
-    fp32 terms, a fp32 norm and rotation stay well below 2^-16 of it."""
-    a = np.abs(ref)
-    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    rms = float(np.sqrt(np.mean(ref ** 2)))
-    return 2.0 ** (e - 8) + rel * (a + rms) + 1e-30
+_one_rounding = one_rounding
 
 
 @pytest.mark.parametrize("F,L,H,hidden", [(16, 700, 4, 512), (8, 300, 2, 256)])
