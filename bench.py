@@ -24,6 +24,11 @@ that packed layout: timestep MLP, output-head table, patch projections into
 the packed stream, output heads; value is its fp32 TFLOP/s and the roofline
 object is the video patch projection against the fp32 MFMA peak.
 
+With --workload forward_L8192 the step is the whole transformer forward at
+L=8192: timestep MLP, head table, token refiner (2 blocks on the 512 text
+rows), pack, the 50-block stack and the output heads; value is its
+algorithmic TFLOP/s, and a HIP graph of the same step is timed beside it.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--copy-probe BYTES]
 """
@@ -329,6 +334,151 @@ def io_bench(args) -> int:
     return 0
 
 
+def forward_bench(args) -> int:
+    """The whole transformer forward on the L=8192 packed layout: timestep MLP,
+    head table, token refiner (2 blocks over the 512 text rows), pack, 50 DiT
+    blocks, output heads.  Weights are seeded N(0, 0.02^2) bf16 generated on
+    the device (about 67 GB); the fp32 input/output weights come from
+    synth.make_io_inputs.  value = algorithmic TFLOP/s of the whole step;
+    roofline = the fc1 + SwiGLU GEMM (the largest kernel) in its own launches.
+    The step is also captured in a HIP graph and its replays timed."""
+    import numpy as np
+    import torch
+    from packed_masked_attention_amd import binding as B
+    from packed_masked_attention_amd import synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    wl = synth.workload("block_L8192")
+    lay = synth.make_layout(wl)
+    L, hid, H, ffn, E, D = wl.L, wl.hidden, wl.H, wl.ffn, wl.temb_dim, wl.D
+    HD = H * D
+    T = lay["T"]
+    n_blocks, n_ref, text_dim = args.blocks, 2, 5120
+    tidx = lay["text_idx"]
+    nt = int(tidx.size)
+    text_lay = synth.layout_from_tags(np.full(nt, synth.TAG_TEXT, np.int32), lay["pos"][tidx],
+                                      lay["ts_idx"][tidx], T)
+    log(f"[bench] generating forward_L8192 weights ({n_blocks} + {n_ref} blocks)")
+    g = torch.Generator(device=dev).manual_seed(8)
+
+    def rnd(*shape, std=0.02):
+        return (torch.randn(*shape, generator=g, device=dev) * std).to(torch.bfloat16)
+
+    ones = torch.ones(D, dtype=torch.float32, device=dev)
+    keep = []
+
+    def weight_set():
+        t = [rnd(3, 6 * hid, E), rnd(3 * HD, hid), rnd(hid, HD), rnd(2 * ffn, hid), rnd(hid, ffn)]
+        keep.append(t)
+        return B.BlockWeights(*(x.data_ptr() for x in t), ones.data_ptr(), ones.data_ptr())
+
+    blocks = B.block_weights_array([weight_set() for _ in range(n_blocks)])
+    refiner = B.block_weights_array([weight_set() for _ in range(n_ref)])
+    w_text = rnd(hid, text_dim, std=text_dim ** -0.5)
+    d = synth.make_io_inputs(lay, hidden=hid, inner_dim=5376, temb_dim=E)
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    t, w1, b1, w2, b2 = (f(d[k]) for k in ("t", "w1", "b1", "w2", "b2"))
+    w_mod = f(d["w_mod"])
+    video, wv, bv = f(d["video"]), f(d["w_video"]), f(d["b_video"])
+    audio, wa, ba = f(d["audio"]), f(d["w_audio"]), f(d["b_audio"])
+    hw = [f(d[k]) for k in ("w_vout", "b_vout", "w_aout", "b_aout")]
+    text = rnd(nt, text_dim, std=1.0)
+    nv, na = int(lay["video_idx"].size), int(lay["audio_idx"].size)
+    tp, io = B.temb_params(256, 5376, E), B.io_params(hid, time_embed_dim=E)
+    p = B.block_params(hid, ffn, E, H)
+    dl = B.pma_layout_build(lay, device=dev)
+    dlt = B.pma_layout_build(text_lay, device=dev)
+    inner_t = torch.empty(T, 5376, device=dev)
+    temb = torch.empty(T, E, device=dev)
+    temb_b = torch.empty(T, E, dtype=torch.bfloat16, device=dev)
+    table = torch.empty(2, T, 2, hid, device=dev)
+    text_out = torch.empty(nt, hid, dtype=torch.bfloat16, device=dev)
+    x = torch.empty(L, hid, dtype=torch.bfloat16, device=dev).normal_()
+    x2 = torch.empty_like(x)
+    vout = torch.empty(nv, 96, device=dev)
+    aout = torch.empty(na, 32, device=dev)
+    ws_ref = torch.empty(B.pma_refiner_workspace_size(p, nt, T), dtype=torch.uint8, device=dev)
+    ws_stack = torch.empty(B.pma_stack_workspace_size(p, L, T), dtype=torch.uint8, device=dev)
+    ws_io = torch.empty(B.pma_unpack_workspace_size(io, nv, na), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.pma_timestep_embed(tp, T, t, w1, b1, w2, b2, inner_t, temb, temb_b)
+        B.pma_head_table(io, T, temb, w_mod, table)
+        B.pma_text_refiner(p, dlt, refiner, temb_b, text, text_dim, text_dim, w_text, 1e-5,
+                           text_out, ws_ref)
+        B.pma_pack_rows(io, dl, video, wv, bv, audio, wa, ba, text_out, hid, x)
+        B.pma_stack_forward(p, dl, blocks, temb_b, x, x2, ws_stack)
+        B.pma_unpack_rows(io, dl, x2, table, *hw, vout, aout, ws_io)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ref_v = vout.clone()
+    # the same step as one HIP graph
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    graph_same = bool(torch.equal(vout, ref_v))
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms_graph = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    def block_flops(n, tags):
+        attn = attention_flops(tags, H, D)
+        gemm = 2 * n * hid * (3 * HD) + 2 * n * HD * hid + 2 * n * hid * (2 * ffn) + 2 * n * ffn * hid
+        return attn + gemm + 2 * 3 * 6 * hid * E * T
+    io_flops = (2 * T * (256 * 5376 + 5376 * E) + 2 * T * E * 4 * hid
+                + 2 * (nv * 96 + na * 32) * hid * 2)
+    flops = (n_blocks * block_flops(L, lay["tags"]) + n_ref * block_flops(nt, text_lay["tags"])
+             + 2 * nt * text_dim * hid + io_flops)
+    # dominant kernel: fc1 + SwiGLU at L rows, in its own launches on this stream
+    bb = torch.empty(L, hid, dtype=torch.bfloat16, device=dev).normal_()
+    hh = torch.empty(L, ffn, dtype=torch.bfloat16, device=dev)
+    w_fc1 = keep[0][3]
+    for _ in range(3):
+        B.pma_linear(L, ffn, hid, bb, hid, w_fc1, hid, hh, ffn, B.EPI_SWIGLU)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        B.pma_linear(L, ffn, hid, bb, hid, w_fc1, hid, hh, ffn, B.EPI_SWIGLU)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fc1_ms = e0.elapsed_time(e1) / 10
+    achieved = 2 * L * (2 * ffn) * hid / (fc1_ms * 1e-3) / 1e12
+    value = flops / (ms_step * 1e-3) / 1e12
+    outj = {
+        "metric": f"MiniMax-H3 transformer forward TFLOP/s at L=8192 ({n_blocks} blocks + "
+                  f"{n_ref} refiner blocks + input/output path)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "forward_L8192", "seq_len": L, "hidden": hid, "heads": H,
+                   "head_dim": D, "ffn_dim": ffn, "blocks": n_blocks, "refiner_blocks": n_ref,
+                   "text_rows": nt, "text_dim": text_dim, "algorithmic_flops": flops,
+                   "ms_per_step_hip_graph": round(ms_graph, 3),
+                   "hip_graph_output_equal": graph_same,
+                   "pct_bf16_peak_step": round(100 * value / BF16_PEAK_TFLOPS, 2)},
+        "roofline": {"kernel": "gemm_kernel<SWIGLU> (fc1)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "avg_ms": round(fc1_ms, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(outj), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -336,6 +486,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="masked_L16384")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--blocks", type=int, default=50, help="DiT blocks of forward_L8192")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", type=int, default=0, help=argparse.SUPPRESS)
     args = ap.parse_args()
@@ -352,6 +503,8 @@ def main() -> int:
         return block_bench(args)
     if args.workload.startswith("io_"):
         return io_bench(args)
+    if args.workload == "forward_L8192":
+        return forward_bench(args)
 
     import numpy as np
     import torch

@@ -336,6 +336,42 @@ pma_status pma_block_forward(const pma_block_params *p, const pma_layout *layout
                              const pma_bf16 *x_in, pma_bf16 *x_out, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/* Block stack.  [H3] constructor parameters: num_layers (50) blocks, each
+ * with its own weights; [ENG] "Scheduling en activatiegeheugen": one
+ * activation arena serves every block.  Reading: block l gets its own AdaLN
+ * table temb W_ada[l]^T (computed just before it, into the workspace) and the
+ * bf16 residual stream passes from block to block; the RoPE table is built
+ * once per call.  w: host array of num_blocks weight sets (device pointers);
+ * temb: bf16 [T][E] with T = layout->num_timesteps; x_in, x_out: bf16
+ * [L][hidden], distinct.  Workspace: pma_stack_workspace_size, 256-byte
+ * aligned, reused by every block. */
+pma_status pma_stack_workspace_size(const pma_block_params *p, int32_t seq_len,
+                                    int32_t num_timesteps, size_t *bytes);
+pma_status pma_stack_forward(const pma_block_params *p, const pma_layout *layout,
+                             int32_t num_blocks, const pma_block_weights *w,
+                             const pma_bf16 *temb, const pma_bf16 *x_in, pma_bf16 *x_out,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Token refiner.  [H3] constructor parameters: num_refiner_layers (2)
+ * blocks applied to the projected text stream, text_dim (5120) the width of
+ * the text conditioning, final_norm_eps (1e-5) the epsilon of the refiner's
+ * output norm.  Readings: proj = text W_text^T (bf16, no bias, as every
+ * projection of the bf16 stack); then num_blocks blocks (pma_stack_forward)
+ * over the text rows alone, described by text_layout (seq_len = n text rows,
+ * every tag 1, the rows' own positions and timestep indices; built with
+ * pma_layout_build and the attention tiles); then LayerNorm without affine,
+ * eps = final_norm_eps.  text: bf16 [n][text_ld]; w_text: bf16
+ * [hidden][text_dim], text_dim % 64 == 0; out: bf16 [n][hidden] (the rows
+ * pma_pack_rows scatters to the text indices).  num_blocks may be 0. */
+pma_status pma_refiner_workspace_size(const pma_block_params *p, int32_t n_text,
+                                      int32_t num_timesteps, size_t *bytes);
+pma_status pma_text_refiner(const pma_block_params *p, const pma_layout *text_layout,
+                            int32_t num_blocks, const pma_block_weights *w,
+                            const pma_bf16 *temb, const pma_bf16 *text, int64_t text_ld,
+                            int32_t text_dim, const pma_bf16 *w_text, float final_norm_eps,
+                            pma_bf16 *out, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
 /* ======================================================================
  * 4. Input and output path: timestep MLP, row pack, output heads
  * ----------------------------------------------------------------------

@@ -116,6 +116,16 @@ _SIGS = {
     "pma_block_forward": (_i32, [ctypes.POINTER(BlockParams), ctypes.POINTER(Layout),
                                  ctypes.POINTER(BlockWeights), _vp, _vp, _vp, _vp,
                                  ctypes.c_size_t, _vp]),
+    "pma_stack_workspace_size": (_i32, [ctypes.POINTER(BlockParams), _i32, _i32,
+                                        ctypes.POINTER(ctypes.c_size_t)]),
+    "pma_stack_forward": (_i32, [ctypes.POINTER(BlockParams), ctypes.POINTER(Layout), _i32,
+                                 ctypes.POINTER(BlockWeights), _vp, _vp, _vp, _vp,
+                                 ctypes.c_size_t, _vp]),
+    "pma_refiner_workspace_size": (_i32, [ctypes.POINTER(BlockParams), _i32, _i32,
+                                          ctypes.POINTER(ctypes.c_size_t)]),
+    "pma_text_refiner": (_i32, [ctypes.POINTER(BlockParams), ctypes.POINTER(Layout), _i32,
+                                ctypes.POINTER(BlockWeights), _vp, _vp, _i64, _i32, _vp,
+                                ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]),
     "pma_timestep_embed": (_i32, [ctypes.POINTER(TembParams), _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _vp]),
     "pma_pack_rows": (_i32, [ctypes.POINTER(IoParams), ctypes.POINTER(LayoutDesc), _vp, _vp, _vp,
@@ -352,6 +362,53 @@ def pma_block_forward(p: BlockParams, dl: DeviceLayout, w: BlockWeights, table, 
     check(lib().pma_block_forward(ctypes.byref(p), ctypes.byref(dl.struct), ctypes.byref(w),
                                   ptr(table), ptr(x_in), ptr(x_out), ptr(workspace),
                                   workspace.numel(), stream_ptr(stream)))
+
+
+def block_weights_array(ws) -> ctypes.Array:
+    """A C array of BlockWeights from a list of them."""
+    arr = (BlockWeights * len(ws))()
+    for i, w in enumerate(ws):
+        arr[i] = w
+    return arr
+
+
+def pma_stack_workspace_size(p: BlockParams, seq_len: int, num_timesteps: int) -> int:
+    n = ctypes.c_size_t()
+    check(lib().pma_stack_workspace_size(ctypes.byref(p), seq_len, num_timesteps, ctypes.byref(n)))
+    return n.value
+
+
+def pma_stack_forward(p: BlockParams, dl: DeviceLayout, weights, temb, x_in, x_out,
+                      workspace=None, stream=None) -> None:
+    """weights: list of BlockWeights (or a ctypes array of them), one per block."""
+    import torch
+    arr = weights if isinstance(weights, ctypes.Array) else block_weights_array(weights)
+    nbytes = pma_stack_workspace_size(p, dl.seq_len, dl.struct.num_timesteps)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x_in.device)
+    check(lib().pma_stack_forward(ctypes.byref(p), ctypes.byref(dl.struct), len(arr), arr,
+                                  ptr(temb), ptr(x_in), ptr(x_out), ptr(workspace),
+                                  workspace.numel(), stream_ptr(stream)))
+
+
+def pma_refiner_workspace_size(p: BlockParams, n_text: int, num_timesteps: int) -> int:
+    n = ctypes.c_size_t()
+    check(lib().pma_refiner_workspace_size(ctypes.byref(p), n_text, num_timesteps,
+                                           ctypes.byref(n)))
+    return n.value
+
+
+def pma_text_refiner(p: BlockParams, dl_text: DeviceLayout, weights, temb, text, text_ld,
+                     text_dim, w_text, final_norm_eps, out, workspace=None, stream=None) -> None:
+    import torch
+    arr = weights if isinstance(weights, ctypes.Array) else block_weights_array(weights)
+    nbytes = pma_refiner_workspace_size(p, dl_text.seq_len, dl_text.struct.num_timesteps)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=text.device)
+    check(lib().pma_text_refiner(ctypes.byref(p), ctypes.byref(dl_text.struct), len(arr),
+                                 arr if len(arr) else None, ptr(temb), ptr(text), text_ld,
+                                 text_dim, ptr(w_text), final_norm_eps, ptr(out), ptr(workspace),
+                                 workspace.numel(), stream_ptr(stream)))
 
 
 # ------------------------------------------------------- input / output path

@@ -212,10 +212,16 @@ pma_status pma_block_workspace_size(const pma_block_params *p, int32_t L, size_t
     return PMA_OK;
 }
 
-pma_status pma_block_forward(const pma_block_params *p, const pma_layout *layout,
-                             const pma_block_weights *w, const float *table,
-                             const pma_bf16 *x_in, pma_bf16 *x_out, void *workspace,
-                             size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// One block; rope_ready: the workspace's RoPE table already holds this
+// layout's cos/sin (the stack builds it once for all its blocks).
+pma_status block_forward_impl(const pma_block_params *p, const pma_layout *layout,
+                              const pma_block_weights *w, const float *table,
+                              const pma_bf16 *x_in, pma_bf16 *x_out, void *workspace,
+                              size_t workspace_bytes, bool rope_ready, void *stream) {
     pma_status st;
     if ((st = check_block_params(p)) != PMA_OK) return st;
     if (!layout || !w || !table || !x_in || !x_out || !workspace)
@@ -255,7 +261,7 @@ pma_status pma_block_forward(const pma_block_params *p, const pma_layout *layout
     pma_bf16 *qh = static_cast<pma_bf16 *>(attn_ws);
     pma_bf16 *kh = reinterpret_cast<pma_bf16 *>(static_cast<char *>(attn_ws) + one);
     pma_bf16 *vt = reinterpret_cast<pma_bf16 *>(static_cast<char *>(attn_ws) + 2 * one);
-    if ((st = pma_rope_table(&p->attn, layout, rope, stream)) != PMA_OK) return st;
+    if (!rope_ready && (st = pma_rope_table(&p->attn, layout, rope, stream)) != PMA_OK) return st;
     if ((st = pma_qkv_projection(&p->attn, layout, ab, hid, hid, w->w_qkv, w->q_norm_weight,
                                  w->k_norm_weight, rope, qh, kh, vt, stream)) != PMA_OK)
         return st;
@@ -286,6 +292,152 @@ pma_status pma_block_forward(const pma_block_params *p, const pma_layout *layout
     g.R = x1; g.ldr = hid; g.table = table; g.num_timesteps = layout->num_timesteps;
     g.gate_chunk = 5; g.token_tags = layout->token_tags; g.timestep_indices = layout->timestep_indices;
     return pma_linear(&g, stream);
+}
+
+// Byte offset of the RoPE table inside a block workspace.
+size_t block_rope_offset(const pma_block_params *p, int32_t L) {
+    const size_t HD = (size_t)p->attn.num_heads * kHeadDim;
+    size_t attn = 0;
+    pma_attention_workspace_size(&p->attn, L, &attn);
+    return round_up((size_t)L * p->hidden * 2, 256) * 2 + round_up((size_t)L * p->ffn_dim * 2, 256) +
+           round_up((size_t)L * HD * 2, 256) + attn;
+}
+
+size_t table_bytes(const pma_block_params *p, int32_t T) {
+    return round_up((size_t)3 * T * 6 * p->hidden * 4, 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+pma_status pma_block_forward(const pma_block_params *p, const pma_layout *layout,
+                             const pma_block_weights *w, const float *table,
+                             const pma_bf16 *x_in, pma_bf16 *x_out, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    return block_forward_impl(p, layout, w, table, x_in, x_out, workspace, workspace_bytes, false,
+                              stream);
+}
+
+// Stack workspace: block workspace | AdaLN table [3][T][6][hidden] fp32 | x [L][hidden] bf16
+pma_status pma_stack_workspace_size(const pma_block_params *p, int32_t L, int32_t T,
+                                    size_t *bytes) {
+    pma_status st;
+    size_t blk = 0;
+    if ((st = pma_block_workspace_size(p, L, &blk)) != PMA_OK) return st;
+    if (T < 1 || T > adaln_max_t()) FAIL(PMA_ERR_SHAPE, "num_timesteps %d (1..%d)", T, adaln_max_t());
+    *bytes = blk + table_bytes(p, T) + round_up((size_t)L * p->hidden * 2, 256);
+    return PMA_OK;
+}
+
+pma_status pma_stack_forward(const pma_block_params *p, const pma_layout *layout,
+                             int32_t num_blocks, const pma_block_weights *w,
+                             const pma_bf16 *temb, const pma_bf16 *x_in, pma_bf16 *x_out,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    pma_status st;
+    if ((st = check_block_params(p)) != PMA_OK) return st;
+    if ((st = api_check_layout(layout)) != PMA_OK) return st;
+    if (num_blocks < 1) FAIL(PMA_ERR_SHAPE, "num_blocks %d", num_blocks);
+    if (!w || !temb || !x_in || !x_out || !workspace)
+        FAIL(PMA_ERR_NULL, "weights, temb, x_in, x_out and workspace are required");
+    if (x_in == x_out) FAIL(PMA_ERR_SHAPE, "x_out must not alias x_in");
+    for (int32_t l = 0; l < num_blocks; ++l)
+        if (!w[l].w_ada || !w[l].w_qkv || !w[l].w_o || !w[l].w_fc1 || !w[l].w_fc2 ||
+            !w[l].q_norm_weight || !w[l].k_norm_weight)
+            FAIL(PMA_ERR_NULL, "a weight of block %d is NULL", l);
+    const int32_t L = layout->seq_len, T = layout->num_timesteps;
+    size_t need = 0, blk = 0;
+    if ((st = pma_stack_workspace_size(p, L, T, &need)) != PMA_OK) return st;
+    if ((st = pma_block_workspace_size(p, L, &blk)) != PMA_OK) return st;
+    if (workspace_bytes < need)
+        FAIL(PMA_ERR_WORKSPACE, "stack workspace %zu < %zu bytes", workspace_bytes, need);
+    if (!aligned(workspace, 256)) FAIL(PMA_ERR_ALIGN, "workspace must be 256-byte aligned");
+    char *ws = static_cast<char *>(workspace);
+    float *table = reinterpret_cast<float *>(ws + blk);
+    pma_bf16 *tmp = reinterpret_cast<pma_bf16 *>(ws + blk + table_bytes(p, T));
+    // the RoPE table depends only on the layout: built once for every block
+    float *rope = reinterpret_cast<float *>(ws + block_rope_offset(p, L));
+    if ((st = pma_rope_table(&p->attn, layout, rope, stream)) != PMA_OK) return st;
+    // block l writes x_out when (num_blocks - 1 - l) is even, tmp otherwise,
+    // so the last block lands in x_out and no block reads what it writes
+    const pma_bf16 *src = x_in;
+    for (int32_t l = 0; l < num_blocks; ++l) {
+        pma_bf16 *dst = ((num_blocks - 1 - l) % 2 == 0) ? x_out : tmp;
+        if ((st = pma_adaln_table(p, T, temb, w[l].w_ada, table, stream)) != PMA_OK) return st;
+        if ((st = block_forward_impl(p, layout, &w[l], table, src, dst, workspace, blk, true,
+                                     stream)) != PMA_OK)
+            return st;
+        src = dst;
+    }
+    return PMA_OK;
+}
+
+// Refiner workspace: projected text [n][hidden] bf16 | stack workspace
+pma_status pma_refiner_workspace_size(const pma_block_params *p, int32_t n, int32_t T,
+                                      size_t *bytes) {
+    pma_status st;
+    size_t stack = 0;
+    if ((st = pma_stack_workspace_size(p, n, T, &stack)) != PMA_OK) return st;
+    *bytes = round_up((size_t)n * p->hidden * 2, 256) + stack;
+    return PMA_OK;
+}
+
+pma_status pma_text_refiner(const pma_block_params *p, const pma_layout *text_layout,
+                            int32_t num_blocks, const pma_block_weights *w,
+                            const pma_bf16 *temb, const pma_bf16 *text, int64_t text_ld,
+                            int32_t text_dim, const pma_bf16 *w_text, float final_norm_eps,
+                            pma_bf16 *out, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+    pma_status st;
+    if ((st = check_block_params(p)) != PMA_OK) return st;
+    if ((st = api_check_layout(text_layout)) != PMA_OK) return st;
+    if (num_blocks < 0) FAIL(PMA_ERR_SHAPE, "num_blocks %d", num_blocks);
+    if (!text || !w_text || !out || !workspace) FAIL(PMA_ERR_NULL, "text, w_text, out and workspace are required");
+    if (num_blocks > 0 && (!w || !temb)) FAIL(PMA_ERR_NULL, "block weights and temb are required");
+    if (text_dim < 64 || text_dim % 64 != 0 || text_ld < text_dim || text_ld % 8 != 0)
+        FAIL(PMA_ERR_SHAPE, "text_dim %d (multiple of 64), text_ld %lld", text_dim, (long long)text_ld);
+    if (!(final_norm_eps >= 0.f)) FAIL(PMA_ERR_SHAPE, "final_norm_eps %g", (double)final_norm_eps);
+    if (!aligned(text, 16) || !aligned(w_text, 16) || !aligned(out, 16))
+        FAIL(PMA_ERR_ALIGN, "text, w_text and out must be 16-byte aligned");
+    const int32_t n = text_layout->seq_len, T = text_layout->num_timesteps;
+    size_t need = 0;
+    if ((st = pma_refiner_workspace_size(p, n, T, &need)) != PMA_OK) return st;
+    if (workspace_bytes < need)
+        FAIL(PMA_ERR_WORKSPACE, "refiner workspace %zu < %zu bytes", workspace_bytes, need);
+    if (!aligned(workspace, 256)) FAIL(PMA_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (!fits32(n, text_ld) || !fits32(p->hidden, text_dim)) FAIL(PMA_ERR_SHAPE, "text spans 2 GiB or more");
+    char *ws = static_cast<char *>(workspace);
+    pma_bf16 *proj = reinterpret_cast<pma_bf16 *>(ws);
+    const size_t proj_bytes = round_up((size_t)n * p->hidden * 2, 256);
+    // text projection (bf16 stack, no bias)
+    pma_linear_args g;
+    memset(&g, 0, sizeof g);
+    g.M = n; g.N = p->hidden; g.K = text_dim;
+    g.A = text; g.lda = text_ld; g.W = w_text; g.ldw = text_dim; g.C = proj; g.ldc = p->hidden;
+    g.epilogue = PMA_EPI_STORE;
+    if ((st = pma_linear(&g, stream)) != PMA_OK) return st;
+    const pma_bf16 *last = proj;
+    if (num_blocks > 0) {
+        if ((st = pma_stack_forward(p, text_layout, num_blocks, w, temb, proj, out, ws + proj_bytes,
+                                    workspace_bytes - proj_bytes, stream)) != PMA_OK)
+            return st;
+        last = out;
+    }
+    // output norm: LayerNorm without modulation, eps = final_norm_eps (in place when
+    // the blocks already wrote out)
+    LnModLaunch a;
+    memset(&a, 0, sizeof a);
+    a.L = n;
+    a.hidden = p->hidden;
+    a.T = T;
+    a.eps = final_norm_eps;
+    a.x = last;
+    a.out = out;
+    a.table = nullptr;
+    a.tags = text_layout->token_tags;
+    a.ts_idx = text_layout->timestep_indices;
+    CHECK_HIP(launch_ln_modulate(a, static_cast<hipStream_t>(stream)), "refiner norm launch");
+    return PMA_OK;
 }
 
 }  // extern "C"

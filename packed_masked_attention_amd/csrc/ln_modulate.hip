@@ -6,7 +6,8 @@
 // forward parameters -- token_tags and timestep_indices per row.
 // Readings: LayerNorm without affine (population variance), then
 // u * (1 + scale) + shift with (shift, scale) = table[tag][ts][chunk];
-// padding rows (tag -1) use zero modulation.
+// padding rows (tag -1) use zero modulation; without a table (the token
+// refiner's output norm) every row is normalised only.
 //
 // HBM-bound: one 256-thread block per row reads the row once (kept in
 // registers for both passes of the mean/variance), gathers the two fp32
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void ln_modulate_kernel(LnModLaunch a) {
     const float rstd = 1.0f / sqrtf(var + a.eps);
     const int tag = a.tags[row], ts = a.ts_idx[row];
     const float *shift = nullptr, *scale = nullptr;
-    if (tag >= 0 && tag <= 2 && (uint32_t)ts < (uint32_t)a.T) {
+    if (a.table && tag >= 0 && tag <= 2 && (uint32_t)ts < (uint32_t)a.T) {
         const int64_t base = (int64_t)(tag * a.T + ts) * 6;
         shift = a.table + (base + a.shift_chunk) * a.hidden;
         scale = a.table + (base + a.shift_chunk + 1) * a.hidden;

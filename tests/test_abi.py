@@ -122,3 +122,32 @@ def test_io_path_host_side_argument_errors(lib):
                                   fake, None, None) == 2
     assert lib.pma_head_table(ctypes.byref(p), 0, fake, fake, fake, None) == 2
     assert lib.pma_head_table(ctypes.byref(p), 1, ctypes.c_void_p(260), fake, fake, None) == 3
+
+
+def test_stack_and_refiner_host_side_argument_errors(lib):
+    n = ctypes.c_size_t()
+    fake = ctypes.c_void_p(256)
+    p = B.block_params(5376, 14336, 2688, 56)
+    blk = ctypes.c_size_t()
+    assert lib.pma_block_workspace_size(ctypes.byref(p), 8192, ctypes.byref(blk)) == 0
+    assert lib.pma_stack_workspace_size(ctypes.byref(p), 8192, 1, ctypes.byref(n)) == 0
+    # block workspace + AdaLN table [3][1][6][5376] fp32 + one residual buffer
+    assert n.value == blk.value + 3 * 6 * 5376 * 4 + 8192 * 5376 * 2
+    assert lib.pma_stack_workspace_size(ctypes.byref(p), 8192, 0, ctypes.byref(n)) == 2
+    lay = B.Layout(8192, 1, 256, 64, 32, 128, fake, fake, fake, fake, fake, fake, fake, fake,
+                   fake, fake)
+    w = B.block_weights_array([B.BlockWeights(256, 256, 256, 256, 256, 256, 256)])
+    assert lib.pma_stack_forward(ctypes.byref(p), ctypes.byref(lay), 0, w, fake, fake,
+                                 ctypes.c_void_p(512), fake, 1 << 40, None) == 2
+    assert lib.pma_stack_forward(ctypes.byref(p), ctypes.byref(lay), 1, w, fake, fake, fake,
+                                 fake, 1 << 40, None) == 2          # x_out aliases x_in
+    w0 = B.block_weights_array([B.BlockWeights(256, 256, None, 256, 256, 256, 256)])
+    assert lib.pma_stack_forward(ctypes.byref(p), ctypes.byref(lay), 1, w0, fake, fake,
+                                 ctypes.c_void_p(512), fake, 1 << 40, None) == 1
+    assert lib.pma_stack_forward(ctypes.byref(p), ctypes.byref(lay), 1, w, fake, fake,
+                                 ctypes.c_void_p(512), fake, 1024, None) == 4
+    assert lib.pma_refiner_workspace_size(ctypes.byref(p), 512, 1, ctypes.byref(n)) == 0
+    assert lib.pma_text_refiner(ctypes.byref(p), ctypes.byref(lay), 2, w, fake, fake, 5120, 5000,
+                                fake, ctypes.c_float(1e-5), fake, fake, 1 << 40, None) == 2
+    assert lib.pma_text_refiner(ctypes.byref(p), ctypes.byref(lay), 2, w, fake, fake, 5120, 5120,
+                                fake, ctypes.c_float(-1.0), fake, fake, 1 << 40, None) == 2
