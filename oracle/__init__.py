@@ -75,7 +75,7 @@ def lib():
             L.oracle_qk_norm_rope.argtypes = [
                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                 ctypes.c_double, ctypes.c_double, _f64p, ctypes.c_int64, _f64p,
-                _i32p, _f64p]
+                _i32p, _f64p, _f64p]
             for name, p in (("oracle_attention_f64", _f64p), ("oracle_attention_f32", _f32p)):
                 fn = getattr(L, name)
                 fn.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, p, p, p,
@@ -167,8 +167,9 @@ def inv_freq(F: int, theta: float) -> np.ndarray:
 
 
 def qk_norm_rope(x: np.ndarray, H: int, D: int, weight, pos, F: int = 16,
-                 theta: float = 10000.0, eps: float = 1e-5) -> np.ndarray:
+                 theta: float = 10000.0, eps: float = 1e-5, pos_scale=None) -> np.ndarray:
     """x: bf16 bits (uint16) or real values, [L, ld] (ld >= H*D) or [L, H, D].
+    pos_scale: per-axis scale of the (t, h, w) coordinates (None = 1, 1, 1).
     Returns fp64 [L, H, D]."""
     x = np.asarray(x)
     x = bf16_to_f64(x) if x.dtype == np.uint16 else np.ascontiguousarray(x, np.float64)
@@ -179,8 +180,10 @@ def qk_norm_rope(x: np.ndarray, H: int, D: int, weight, pos, F: int = 16,
     w = np.ascontiguousarray(np.broadcast_to(np.asarray(weight, np.float64), (D,)))
     p = _i32(pos).reshape(L, 3)
     y = np.empty((L, H, D), dtype=np.float64)
+    sc = None if pos_scale is None else np.ascontiguousarray(pos_scale, dtype=np.float64).reshape(3)
     lib().oracle_qk_norm_rope(L, H, D, F, float(theta), float(eps), _ptr(x2, _f64p), ld,
-                              _ptr(w, _f64p), _ptr(p, _i32p), _ptr(y, _f64p))
+                              _ptr(w, _f64p), _ptr(p, _i32p),
+                              None if sc is None else _ptr(sc, _f64p), _ptr(y, _f64p))
     return y
 
 
@@ -208,7 +211,8 @@ def attention(q, k, v, tags, rows=None, scale=None, precision="f64"):
 
 def attention_path(q_bits, k_bits, v_bits, layout: dict, H: int, D: int = 128,
                    rows=None, wq=1.0, wk=1.0, F: int = 16, theta: float = 10000.0,
-                   eps: float = 1e-5, store_qk_bf16: bool = False, precision="f64"):
+                   eps: float = 1e-5, store_qk_bf16: bool = False, precision="f64",
+                   pos_scale=None):
     """QK-RMSNorm + 3-axis RoPE on Q and K, then masked attention.
 
     Inputs are bf16 bit arrays [L, H, D] (or [L, ld] with head h at column h*D).
@@ -218,8 +222,8 @@ def attention_path(q_bits, k_bits, v_bits, layout: dict, H: int, D: int = 128,
     """
     L = np.asarray(q_bits).shape[0]
     pos = layout["pos"]
-    qn = qk_norm_rope(q_bits, H, D, wq, pos, F, theta, eps)
-    kn = qk_norm_rope(k_bits, H, D, wk, pos, F, theta, eps)
+    qn = qk_norm_rope(q_bits, H, D, wq, pos, F, theta, eps, pos_scale)
+    kn = qk_norm_rope(k_bits, H, D, wk, pos, F, theta, eps, pos_scale)
     if store_qk_bf16:
         qn = bf16_storage(qn)
         kn = bf16_storage(kn)

@@ -77,7 +77,8 @@ def silu(z):
 def block_forward(inp: dict, rows=None, store_bf16: bool = True, eps: float = 1e-5,
                   qk_eps: float = 1e-5, F: int = 16, theta: float = 10000.0,
                   wq=1.0, wk=1.0, mod: np.ndarray | None = None,
-                  return_intermediates: bool = False, fused_qkv: bool = False):
+                  return_intermediates: bool = False, fused_qkv: bool = False,
+                  pos_scale=None):
     """x2 for the listed rows (all rows when ``rows`` is None).
 
     ``fused_qkv``: the QKV projection hands its Q and K columns straight to
@@ -104,8 +105,8 @@ def block_forward(inp: dict, rows=None, store_bf16: bool = True, eps: float = 1e
     # the attention path on stored bf16 Q, K, V
     q_all = np.zeros((L, HD))
     q_all[rows] = qr
-    qn = qk_norm_rope(q_all, H, D, wq, lay["pos"], F, theta, qk_eps)
-    kn = qk_norm_rope(kv[:, :HD], H, D, wk, lay["pos"], F, theta, qk_eps)
+    qn = qk_norm_rope(q_all, H, D, wq, lay["pos"], F, theta, qk_eps, pos_scale)
+    kn = qk_norm_rope(kv[:, :HD], H, D, wk, lay["pos"], F, theta, qk_eps, pos_scale)
     if store_bf16:
         qn, kn = bf16_storage(qn), bf16_storage(kn)
     v = kv[:, HD:].reshape(L, H, D)

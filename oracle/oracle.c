@@ -224,13 +224,17 @@ void oracle_inv_freq(int32_t F, double theta, double *inv_freq)
  * x: [L][ld] values with head h of row i at x[i*ld + h*D + c].
  * y: fp64 [L][H][D].  For every (row, head):
  *   r = 1/sqrt(mean_c x_c^2 + eps);  n_c = x_c * r * w[c]
- *   for axis a, f < F: phi = pos[i][a]*inv_freq[f]; c0 = 2aF+f; c1 = c0+F
+ *   for axis a, f < F: phi = (pos[i][a] * pos_scale[a]) * inv_freq[f];
+ *     c0 = 2aF+f; c1 = c0+F
  *     y_c0 = n_c0 cos phi - n_c1 sin phi;  y_c1 = n_c1 cos phi + n_c0 sin phi
  *   y_c = n_c for c >= 6F.
+ * pos_scale (3 values; NULL = all 1) scales each axis' coordinate: the
+ * engine page's 256x256 preview halves the spatial (h, w) coordinates, which
+ * makes the effective positions fractional.
  */
 void oracle_qk_norm_rope(int32_t L, int32_t H, int32_t D, int32_t F, double theta,
                          double eps, const double *x, int64_t ld, const double *w,
-                         const int32_t *pos, double *y)
+                         const int32_t *pos, const double *pos_scale, double *y)
 {
     double inv_freq[64];
     oracle_inv_freq(F, theta, inv_freq);
@@ -248,7 +252,7 @@ void oracle_qk_norm_rope(int32_t L, int32_t H, int32_t D, int32_t F, double thet
         for (int32_t c = 0; c < D; ++c) n[c] = xr[c] * r * w[c];
         for (int32_t c = 0; c < D; ++c) yr[c] = n[c];
         for (int32_t a = 0; a < 3; ++a) {
-            double p = (double)pos[3 * i + a];
+            double p = (double)pos[3 * i + a] * (pos_scale ? pos_scale[a] : 1.0);
             for (int32_t f = 0; f < F; ++f) {
                 double phi = p * inv_freq[f];
                 int32_t c0 = 2 * a * F + f, c1 = c0 + F;

@@ -116,6 +116,32 @@ def test_rope_matches_complex_rotation():
     assert np.allclose(y, _complex_rope_reference(n, pos), rtol=1e-12, atol=1e-12)
 
 
+def test_rope_scaled_coordinates():
+    """The engine page's 256x256 preview halves the spatial coordinates: with
+    scale (1, 1/2, 1/2), doubled spatial positions give exactly the unscaled
+    result, and odd ones land halfway (fractional positions), matching the
+    complex rotation at those fractional positions."""
+    x = _rand_qk(L=40, H=2)
+    L, H, D = x.shape
+    rng = np.random.default_rng(8)
+    pos = rng.integers(0, 300, (L, 3)).astype(np.int32)
+    sc = (1.0, 0.5, 0.5)
+    doubled = pos.copy()
+    doubled[:, 1:] *= 2
+    assert np.array_equal(oracle.qk_norm_rope(x, H, D, 1.0, doubled, pos_scale=sc),
+                          oracle.qk_norm_rope(x, H, D, 1.0, pos))
+    odd = pos.copy()
+    odd[:, 1:] = 2 * odd[:, 1:] + 1
+    n = oracle.qk_norm_rope(x, H, D, 1.0, np.zeros((L, 3), np.int32))
+    y = oracle.qk_norm_rope(x, H, D, 1.0, odd, pos_scale=sc)
+    frac = pos.astype(np.float64)
+    frac[:, 1:] += 0.5
+    assert np.allclose(y, _complex_rope_reference(n, frac), rtol=1e-12, atol=1e-12)
+    # the temporal axis keeps its integer positions
+    assert np.array_equal(oracle.qk_norm_rope(x, H, D, 1.0, odd, pos_scale=sc)[..., :32],
+                          oracle.qk_norm_rope(x, H, D, 1.0, odd)[..., :32])
+
+
 def test_rope_temporal_only_is_textbook_1d_rope():
     x = _rand_qk(L=30, H=2)
     L, H, D = x.shape
