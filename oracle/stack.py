@@ -28,7 +28,7 @@ from .block import adaln_table, block_forward, layer_norm
 
 
 def stack_forward(x_bits, temb_bits, blocks, layout, dims: dict, store_bf16: bool = True,
-                  fused_qkv: bool = True, eps: float = 1e-5) -> np.ndarray:
+                  fused_qkv: bool = True, eps: float = 1e-5, pos_scale=None) -> np.ndarray:
     """x after len(blocks) blocks, as bf16 bits [L, hidden].
 
     blocks: list of dicts with w_ada, w_qkv, w_o, w_fc1, w_fc2 (bf16 bits).
@@ -41,7 +41,8 @@ def stack_forward(x_bits, temb_bits, blocks, layout, dims: dict, store_bf16: boo
         inp.update(w)
         inp.update(layout=layout, x=x, temb=temb_bits)
         xv = block_forward(inp, store_bf16=store_bf16, eps=eps,
-                           mod=adaln_table(temb_bits, w["w_ada"]), fused_qkv=fused_qkv)
+                           mod=adaln_table(temb_bits, w["w_ada"]), fused_qkv=fused_qkv,
+                           pos_scale=pos_scale)
         x = bf16_round(xv)
     return x
 
@@ -56,3 +57,26 @@ def text_refiner(text_bits, w_text_bits, temb_bits, blocks, text_layout, dims: d
         x = stack_forward(x, temb_bits, blocks, text_layout, dims, store_bf16=store_bf16, eps=eps)
     y = layer_norm(bf16_to_f64(x), final_eps)
     return bf16_round(y) if store_bf16 else y
+
+
+def reduced_stack_forward(x_bits, temb_bits, blocks, layout, plan: dict, merge_after: int,
+                          restore_before: int, dims: dict, store_bf16: bool = True,
+                          eps: float = 1e-5) -> np.ndarray:
+    """The stack with token reduction (engine page, token-reduction notes):
+    blocks [0, merge_after) at full resolution, merge, blocks
+    [merge_after, restore_before) on the reduced rows (plan["layout"], its
+    positions scaled by plan["pos_scale"]), restore from the bypass, then the
+    remaining blocks at full resolution.  dims' L is the full row count."""
+    from .tokenred import merge, unmerge
+    x = stack_forward(x_bits, temb_bits, blocks[:merge_after], layout, dims, store_bf16,
+                      eps=eps) if merge_after else np.asarray(x_bits, np.uint16)
+    bypass = x
+    xr0 = merge(x, plan["src0"], plan["src1"])
+    rdims = dict(dims)
+    rdims["L"] = int(plan["layout"]["L"])
+    xr1 = stack_forward(xr0, temb_bits, blocks[merge_after:restore_before], plan["layout"], rdims,
+                        store_bf16, eps=eps, pos_scale=plan["pos_scale"])
+    x = unmerge(bypass, xr0, xr1, plan["src0"], plan["src1"])
+    if restore_before < len(blocks):
+        x = stack_forward(x, temb_bits, blocks[restore_before:], layout, dims, store_bf16, eps=eps)
+    return x

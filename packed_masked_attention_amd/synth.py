@@ -207,6 +207,42 @@ def make_block_inputs(L: int, hidden: int, heads: int, head_dim: int, ffn: int,
             "heads": heads, "head_dim": head_dim, "ffn": ffn, "temb_dim": temb_dim}
 
 
+def token_reduction_plan(layout: dict, target_ts=None) -> dict:
+    """Pair horizontally adjacent target-video rows of a packed layout.
+
+    Layout construction only (the caller's job): rows are taken in sequence
+    order; a video row at (t, h, 2j) whose next row is the video row at
+    (t, h, 2j + 1) forms a pair when both are target rows (timestep index
+    == target_ts, or every video row when target_ts is None).  Every other
+    row stays on its own.  Returns src0/src1 ([n_reduced], src1 = -1 for an
+    unpaired row) and the reduced layout, whose positions are in half units
+    (every coordinate doubled; a pair sits at w = 4j + 1, i.e. 2j + 1/2 in
+    full units), to be used with a position scale of 1/2 on every axis."""
+    tags, pos, ts = layout["tags"], layout["pos"], layout["ts_idx"]
+    L = tags.size
+    target = (tags == TAG_VIDEO) & ((ts == target_ts) if target_ts is not None else True)
+    src0, src1 = [], []
+    i = 0
+    while i < L:
+        if (i + 1 < L and target[i] and target[i + 1] and pos[i, 2] % 2 == 0
+                and pos[i + 1, 0] == pos[i, 0] and pos[i + 1, 1] == pos[i, 1]
+                and pos[i + 1, 2] == pos[i, 2] + 1):
+            src0.append(i)
+            src1.append(i + 1)
+            i += 2
+        else:
+            src0.append(i)
+            src1.append(-1)
+            i += 1
+    src0 = np.asarray(src0, np.int32)
+    src1 = np.asarray(src1, np.int32)
+    rpos = 2 * pos[src0].astype(np.int64)
+    paired = src1 >= 0
+    rpos[paired, 2] += 1
+    red = layout_from_tags(tags[src0], rpos.astype(np.int32), ts[src0], layout["T"])
+    return {"src0": src0, "src1": src1, "layout": red, "pos_scale": (0.5, 0.5, 0.5)}
+
+
 def normal_f32(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
     return (rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std)).astype(np.float32)
 
