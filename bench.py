@@ -402,6 +402,36 @@ def forward_bench(args) -> int:
     ws_stack = torch.empty(B.pma_stack_workspace_size(p, L, T), dtype=torch.uint8, device=dev)
     ws_io = torch.empty(B.pma_unpack_workspace_size(io, nv, na), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    # token reduction (engine page): blocks 1-3 at full resolution, the target
+    # video rows paired for blocks 4-39, restored from the bypass before block 40
+    red = None
+    if args.token_reduction and n_blocks < 40:
+        log("--token-reduction restores before block 40: it needs --blocks 40 or more")
+        return 2
+    if args.token_reduction:
+        plan = synth.token_reduction_plan(lay)
+        s0 = torch.from_numpy(plan["src0"]).to(dev)
+        s1 = torch.from_numpy(plan["src1"]).to(dev)
+        nr = int(plan["src0"].size)
+        red = {"plan": plan, "s0": s0, "s1": s1, "n": nr, "a": 3, "b": min(39, n_blocks),
+               "dl": B.pma_layout_build(plan["layout"], device=dev),
+               "p": B.block_params(hid, ffn, E, H, pos_scale=plan["pos_scale"]),
+               "xr0": torch.empty(nr, hid, dtype=torch.bfloat16, device=dev),
+               "xr1": torch.empty(nr, hid, dtype=torch.bfloat16, device=dev),
+               "x1": torch.empty_like(x)}
+        blist = list(blocks)
+
+    def run_stack():
+        if red is None:
+            B.pma_stack_forward(p, dl, blocks, temb_b, x, x2, ws_stack)
+            return
+        r = red
+        B.pma_stack_forward(p, dl, blist[:r["a"]], temb_b, x, r["x1"], ws_stack)
+        B.pma_token_merge(hid, L, r["s0"], r["s1"], r["x1"], r["xr0"])
+        B.pma_stack_forward(r["p"], r["dl"], blist[r["a"]:r["b"]], temb_b, r["xr0"], r["xr1"],
+                            ws_stack)
+        B.pma_token_restore(hid, L, r["s0"], r["s1"], r["x1"], r["xr0"], r["xr1"], r["x1"])
+        B.pma_stack_forward(p, dl, blist[r["b"]:], temb_b, r["x1"], x2, ws_stack)
 
     def step():
         B.pma_timestep_embed(tp, T, t, w1, b1, w2, b2, inner_t, temb, temb_b)
@@ -409,7 +439,7 @@ def forward_bench(args) -> int:
         B.pma_text_refiner(p, dlt, refiner, temb_b, text, text_dim, text_dim, w_text, 1e-5,
                            text_out, ws_ref)
         B.pma_pack_rows(io, dl, video, wv, bv, audio, wa, ba, text_out, hid, x)
-        B.pma_stack_forward(p, dl, blocks, temb_b, x, x2, ws_stack)
+        run_stack()
         B.pma_unpack_rows(io, dl, x2, table, *hw, vout, aout, ws_io)
 
     for _ in range(args.warmup):
@@ -440,7 +470,13 @@ def forward_bench(args) -> int:
         return attn + gemm + 2 * 3 * 6 * hid * E * T
     io_flops = (2 * T * (256 * 5376 + 5376 * E) + 2 * T * E * 4 * hid
                 + 2 * (nv * 96 + na * 32) * hid * 2)
-    flops = (n_blocks * block_flops(L, lay["tags"]) + n_ref * block_flops(nt, text_lay["tags"])
+    if red is None:
+        stack_flops = n_blocks * block_flops(L, lay["tags"])
+    else:
+        n_red = red["b"] - red["a"]
+        stack_flops = ((n_blocks - n_red) * block_flops(L, lay["tags"])
+                       + n_red * block_flops(red["n"], red["plan"]["layout"]["tags"]))
+    flops = (stack_flops + n_ref * block_flops(nt, text_lay["tags"])
              + 2 * nt * text_dim * hid + io_flops)
     # dominant kernel: fc1 + SwiGLU at L rows, in its own launches on this stream
     bb = torch.empty(L, hid, dtype=torch.bfloat16, device=dev).normal_()
@@ -459,13 +495,17 @@ def forward_bench(args) -> int:
     value = flops / (ms_step * 1e-3) / 1e12
     outj = {
         "metric": f"MiniMax-H3 transformer forward TFLOP/s at L=8192 ({n_blocks} blocks + "
-                  f"{n_ref} refiner blocks + input/output path)",
+                  f"{n_ref} refiner blocks + input/output path"
+                  + (", token reduction)" if red else ")"),
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "forward_L8192", "seq_len": L, "hidden": hid, "heads": H,
                    "head_dim": D, "ffn_dim": ffn, "blocks": n_blocks, "refiner_blocks": n_ref,
                    "text_rows": nt, "text_dim": text_dim, "algorithmic_flops": flops,
+                   "token_reduction": None if red is None else {
+                       "reduced_rows": red["n"], "full_blocks_before": red["a"],
+                       "reduced_blocks": red["b"] - red["a"], "restored_before_block": red["b"] + 1},
                    "ms_per_step_hip_graph": round(ms_graph, 3),
                    "hip_graph_output_equal": graph_same,
                    "pct_bf16_peak_step": round(100 * value / BF16_PEAK_TFLOPS, 2)},
@@ -487,6 +527,8 @@ def main() -> int:
     ap.add_argument("--workload", default="masked_L16384")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--blocks", type=int, default=50, help="DiT blocks of forward_L8192")
+    ap.add_argument("--token-reduction", action="store_true",
+                    help="forward_L8192 with the engine's token reduction (blocks 4-39 paired)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", type=int, default=0, help=argparse.SUPPRESS)
     args = ap.parse_args()

@@ -150,7 +150,7 @@ pma_status pma_layout_read_status(const pma_layout *layout, void *stream, int32_
  *
  * Computed, per row i and head h (readings of the pages' open points):
  *   n = x * w / sqrt(mean(x^2) + qk_norm_eps)        RMSNorm over the head's D
- *   axis a in {t,h,w}, f < F, phi = pos[i][a] * theta^(-f/F),
+ *   axis a in {t,h,w}, f < F, phi = (pos[i][a] * pos_scale[a]) * theta^(-f/F),
  *   c0 = 2aF + f, c1 = c0 + F:
  *     y[c0] = n[c0] cos phi - n[c1] sin phi,  y[c1] = n[c1] cos phi + n[c0] sin phi
  *   y[c] = n[c] for c >= 6F.
@@ -164,6 +164,10 @@ typedef struct {
     float rope_theta;      /* > 0                                      */
     float qk_norm_eps;     /* >= 0                                     */
     float softmax_scale;   /* 0 selects 1/sqrt(D)                      */
+    float pos_scale[3];    /* per-axis scale of the (t, h, w) positions in
+                              the rotation angle; 0 selects 1.  [ENG]
+                              256x256 preview: the spatial coordinates are
+                              halved (1, 0.5, 0.5) at the 8x8 token grid   */
 } pma_attn_params;
 
 /* The (tile_m, tile_n) the flash attention kernel needs its layout built with. */
@@ -371,6 +375,29 @@ pma_status pma_text_refiner(const pma_block_params *p, const pma_layout *text_la
                             int32_t text_dim, const pma_bf16 *w_text, float final_norm_eps,
                             pma_bf16 *out, void *workspace, size_t workspace_bytes,
                             void *stream);
+
+/* Token reduction.  [ENG] presets and implementation notes: an optional
+ * mode pairs adjacent horizontal target-video tokens after block 3, keeps
+ * text, audio and reference tokens exact, and restores the full-resolution
+ * state, kept as a bypass, before a later block (block 40 for the first ten
+ * noisy evaluations, block 30 afterwards).  The caller builds the plan (as it
+ * builds every layout): reduced row i stands for full rows src0[i] and
+ * src1[i] (src1[i] = -1: src0[i] alone), every full row named exactly once;
+ * and the reduced layout, whose merged rows sit at w + 1/2 (positions in
+ * half units with pos_scale 1/2 on every axis).  Readings:
+ *   merge:   xr[i] = src1[i] < 0 ? x[src0[i]] : bf16((x[src0[i]] + x[src1[i]]) / 2)
+ *   restore: x_out[r] = bf16(bypass[r] + (xr_after[i] - xr_before[i])) for
+ *            r in {src0[i], src1[i]}: the change the reduced blocks made to
+ *            merged row i goes to both of its rows.
+ * Rows are bf16 [.][hidden], hidden % 8 == 0, 16-byte aligned; x_out may
+ * alias bypass.  Index entries outside [0, seq_len) are skipped. */
+pma_status pma_token_merge(int32_t hidden, int32_t seq_len, int32_t n_reduced,
+                           const int32_t *src0, const int32_t *src1, const pma_bf16 *x,
+                           pma_bf16 *xr, void *stream);
+pma_status pma_token_restore(int32_t hidden, int32_t seq_len, int32_t n_reduced,
+                             const int32_t *src0, const int32_t *src1, const pma_bf16 *bypass,
+                             const pma_bf16 *xr_before, const pma_bf16 *xr_after,
+                             pma_bf16 *x_out, void *stream);
 
 /* ======================================================================
  * 4. Input and output path: timestep MLP, row pack, output heads

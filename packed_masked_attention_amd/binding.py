@@ -51,7 +51,7 @@ class Layout(ctypes.Structure):
 class AttnParams(ctypes.Structure):
     _fields_ = [("num_heads", _i32), ("head_dim", _i32), ("rope_freq_dim", _i32),
                 ("rope_theta", ctypes.c_float), ("qk_norm_eps", ctypes.c_float),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("pos_scale", ctypes.c_float * 3)]
 
 
 class BlockParams(ctypes.Structure):
@@ -126,6 +126,8 @@ _SIGS = {
     "pma_text_refiner": (_i32, [ctypes.POINTER(BlockParams), ctypes.POINTER(Layout), _i32,
                                 ctypes.POINTER(BlockWeights), _vp, _vp, _i64, _i32, _vp,
                                 ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]),
+    "pma_token_merge": (_i32, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "pma_token_restore": (_i32, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "pma_timestep_embed": (_i32, [ctypes.POINTER(TembParams), _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _vp]),
     "pma_pack_rows": (_i32, [ctypes.POINTER(IoParams), ctypes.POINTER(LayoutDesc), _vp, _vp, _vp,
@@ -264,8 +266,8 @@ def layout_arrays(dl: DeviceLayout) -> dict:
 # --------------------------------------------------------------- attention
 
 def attn_params(H: int, D: int = 128, F: int = 16, theta: float = 10000.0, eps: float = 1e-5,
-                scale: float = 0.0) -> AttnParams:
-    return AttnParams(H, D, F, theta, eps, scale)
+                scale: float = 0.0, pos_scale=(1.0, 1.0, 1.0)) -> AttnParams:
+    return AttnParams(H, D, F, theta, eps, scale, (ctypes.c_float * 3)(*pos_scale))
 
 
 def pma_attention_tiles() -> tuple[int, int]:
@@ -409,6 +411,18 @@ def pma_text_refiner(p: BlockParams, dl_text: DeviceLayout, weights, temb, text,
                                  arr if len(arr) else None, ptr(temb), ptr(text), text_ld,
                                  text_dim, ptr(w_text), final_norm_eps, ptr(out), ptr(workspace),
                                  workspace.numel(), stream_ptr(stream)))
+
+
+def pma_token_merge(hidden: int, seq_len: int, src0, src1, x, xr, stream=None) -> None:
+    check(lib().pma_token_merge(hidden, seq_len, src0.numel(), ptr(src0), ptr(src1), ptr(x),
+                                ptr(xr), stream_ptr(stream)))
+
+
+def pma_token_restore(hidden: int, seq_len: int, src0, src1, bypass, xr_before, xr_after, x_out,
+                      stream=None) -> None:
+    check(lib().pma_token_restore(hidden, seq_len, src0.numel(), ptr(src0), ptr(src1),
+                                  ptr(bypass), ptr(xr_before), ptr(xr_after), ptr(x_out),
+                                  stream_ptr(stream)))
 
 
 # ------------------------------------------------------- input / output path

@@ -94,6 +94,9 @@ pma_status check_attn_params(const pma_attn_params *p) {
         return fail(PMA_ERR_SHAPE, "qk_norm_eps %g", (double)p->qk_norm_eps);
     if (!(p->softmax_scale >= 0.f) || !std::isfinite(p->softmax_scale))
         return fail(PMA_ERR_SHAPE, "softmax_scale %g", (double)p->softmax_scale);
+    for (int a = 0; a < 3; ++a)
+        if (!std::isfinite(p->pos_scale[a]))
+            return fail(PMA_ERR_SHAPE, "pos_scale[%d] %g", a, (double)p->pos_scale[a]);
     return PMA_OK;
 }
 
@@ -127,6 +130,14 @@ pma_status api_fail(pma_status s, const char *fmt, ...) {
 }
 pma_status api_check_device() { return check_device(); }
 pma_status api_check_attn_params(const pma_attn_params *p) { return check_attn_params(p); }
+void api_fill_rope(const pma_attn_params *p, PrepLaunch &a) {
+    for (int f = 0; f < 16; ++f)
+        a.inv_freq[f] = f < p->rope_freq_dim
+                            ? std::pow((double)p->rope_theta, -(double)f / (double)p->rope_freq_dim)
+                            : 0.0;
+    for (int ax = 0; ax < 3; ++ax)
+        a.pos_scale[ax] = p->pos_scale[ax] == 0.f ? 1.0 : (double)p->pos_scale[ax];
+}
 pma_status api_check_layout(const pma_layout *l) { return check_layout(l); }
 int32_t api_padded_len(int32_t L) { return padded_len(L); }
 }  // namespace pma
@@ -277,8 +288,7 @@ pma_status pma_qk_norm_rope(const pma_attn_params *p, const pma_layout *layout,
     a.H = H;
     a.F = p->rope_freq_dim;
     a.eps = p->qk_norm_eps;
-    for (int f = 0; f < 16; ++f)
-        a.inv_freq[f] = f < a.F ? std::pow((double)p->rope_theta, -(double)f / (double)a.F) : 0.0;
+    api_fill_rope(p, a);
     a.q = q; a.k = k; a.v = v;
     a.q_ld = q_ld; a.k_ld = k_ld; a.v_ld = v_ld;
     a.wq = q_norm_weight; a.wk = k_norm_weight;

@@ -18,6 +18,7 @@ pma_status api_check_device();
 pma_status api_check_attn_params(const pma_attn_params *p);
 pma_status api_check_layout(const pma_layout *l);
 int32_t api_padded_len(int32_t L);
+void api_fill_rope(const pma_attn_params *p, PrepLaunch &a);
 }  // namespace pma
 
 namespace {
@@ -150,8 +151,7 @@ pma_status pma_rope_table(const pma_attn_params *p, const pma_layout *layout, fl
     memset(&a, 0, sizeof a);
     a.L = layout->seq_len;
     a.F = p->rope_freq_dim;
-    for (int f = 0; f < 16; ++f)
-        a.inv_freq[f] = f < a.F ? std::pow((double)p->rope_theta, -(double)f / (double)a.F) : 0.0;
+    api_fill_rope(p, a);
     a.pos = layout->position_ids;
     CHECK_HIP(launch_rope_table(a, reinterpret_cast<float2 *>(table), static_cast<hipStream_t>(stream)),
               "rope table launch");
@@ -369,6 +369,46 @@ pma_status pma_stack_forward(const pma_block_params *p, const pma_layout *layout
             return st;
         src = dst;
     }
+    return PMA_OK;
+}
+
+pma_status pma_token_merge(int32_t hidden, int32_t seq_len, int32_t n_reduced,
+                           const int32_t *src0, const int32_t *src1, const pma_bf16 *x,
+                           pma_bf16 *xr, void *stream) {
+    if (hidden < 8 || hidden % 8 != 0) FAIL(PMA_ERR_SHAPE, "hidden %d (multiple of 8)", hidden);
+    if (seq_len < 1 || n_reduced < 0 || n_reduced > seq_len)
+        FAIL(PMA_ERR_SHAPE, "seq_len %d, n_reduced %d", seq_len, n_reduced);
+    if (n_reduced && (!src0 || !src1 || !x || !xr)) FAIL(PMA_ERR_NULL, "src0, src1, x and xr are required");
+    if (!aligned(x, 16) || !aligned(xr, 16)) FAIL(PMA_ERR_ALIGN, "x and xr must be 16-byte aligned");
+    pma_status st;
+    if ((st = api_check_device()) != PMA_OK) return st;
+    TokenLaunch a;
+    memset(&a, 0, sizeof a);
+    a.n = n_reduced; a.hidden = hidden; a.L = seq_len;
+    a.src0 = src0; a.src1 = src1; a.x = x; a.xr_out = xr;
+    CHECK_HIP(launch_token_merge(a, static_cast<hipStream_t>(stream)), "token merge launch");
+    return PMA_OK;
+}
+
+pma_status pma_token_restore(int32_t hidden, int32_t seq_len, int32_t n_reduced,
+                             const int32_t *src0, const int32_t *src1, const pma_bf16 *bypass,
+                             const pma_bf16 *xr_before, const pma_bf16 *xr_after,
+                             pma_bf16 *x_out, void *stream) {
+    if (hidden < 8 || hidden % 8 != 0) FAIL(PMA_ERR_SHAPE, "hidden %d (multiple of 8)", hidden);
+    if (seq_len < 1 || n_reduced < 0 || n_reduced > seq_len)
+        FAIL(PMA_ERR_SHAPE, "seq_len %d, n_reduced %d", seq_len, n_reduced);
+    if (n_reduced && (!src0 || !src1 || !bypass || !xr_before || !xr_after || !x_out))
+        FAIL(PMA_ERR_NULL, "src0, src1, bypass, xr_before, xr_after and x_out are required");
+    if (!aligned(bypass, 16) || !aligned(xr_before, 16) || !aligned(xr_after, 16) || !aligned(x_out, 16))
+        FAIL(PMA_ERR_ALIGN, "row arrays must be 16-byte aligned");
+    pma_status st;
+    if ((st = api_check_device()) != PMA_OK) return st;
+    TokenLaunch a;
+    memset(&a, 0, sizeof a);
+    a.n = n_reduced; a.hidden = hidden; a.L = seq_len;
+    a.src0 = src0; a.src1 = src1; a.x = bypass; a.xr_before = xr_before; a.xr_in = xr_after;
+    a.x_out = x_out;
+    CHECK_HIP(launch_token_restore(a, static_cast<hipStream_t>(stream)), "token restore launch");
     return PMA_OK;
 }
 

@@ -49,6 +49,7 @@ struct PrepLaunch {
     int32_t L, Lp, H, F;
     float eps;
     double inv_freq[16];
+    double pos_scale[3];    // per-axis scale of the positions (1 = integer positions)
     const uint16_t *q, *k, *v;
     int64_t q_ld, k_ld, v_ld;
     const float *wq, *wk;
@@ -175,6 +176,19 @@ struct HeadLaunch {
 };
 hipError_t launch_head(const HeadLaunch &a, hipStream_t s);
 int head_max_hidden();
+
+// token reduction: merge rows (src0[i], src1[i]) of x into row i of xr_out;
+// restore x_out[r] = x[r] + (xr_in[i] - xr_before[i]) for r in {src0, src1}
+struct TokenLaunch {
+    int32_t n, hidden, L;
+    const int32_t *src0, *src1;
+    const uint16_t *x;          // full rows (merge input / restore bypass)
+    uint16_t *xr_out;           // merge output
+    const uint16_t *xr_before, *xr_in;
+    uint16_t *x_out;            // restore output (may alias x)
+};
+hipError_t launch_token_merge(const TokenLaunch &a, hipStream_t s);
+hipError_t launch_token_restore(const TokenLaunch &a, hipStream_t s);
 int head_max_out();
 int head_max_t();     // distinct timesteps the head kernels accept
 int head_k_chunk();   // each head K range is a multiple of this

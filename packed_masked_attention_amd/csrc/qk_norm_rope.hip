@@ -10,8 +10,10 @@
 //
 // Readings: RMSNorm over the head's 128 channels with one fp32 weight vector
 // shared by all heads; inv_freq[f] = theta^(-f/F); axis a rotates channel
-// pairs (2aF+f, 2aF+f+F) by pos[a]*inv_freq[f] (rotate-half pairing,
-// direction e^{+i phi}); channels >= 6F pass through.
+// pairs (2aF+f, 2aF+f+F) by (pos[a]*pos_scale[a])*inv_freq[f] (rotate-half
+// pairing, direction e^{+i phi}); channels >= 6F pass through.  The per-axis
+// scale is 1 except where the caller asks otherwise (the engine page's
+// 256x256 preview halves the spatial coordinates).
 //
 // HBM-bound: per (row, head) it reads 3 x 256 B and writes 3 x 256 B.
 // Block = 64 rows x 4 heads.  Each 16-lane group owns one (row, head) of Q or
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(PrepLaunch a) {
         float c = 1.f, s = 0.f;
         if (row < a.L) {
             const int ax = j / F, f = j % F;
-            const double phi = (double)a.pos[3 * (int64_t)row + ax] * a.inv_freq[f];
+            const double phi = ((double)a.pos[3 * (int64_t)row + ax] * a.pos_scale[ax]) * a.inv_freq[f];
             double sd, cd;
             sincos(phi, &sd, &cd);
             c = (float)cd;
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(256) void rope_table_kernel(PrepLaunch a, float2 *r
     if (e >= (int64_t)a.L * nang) return;
     const int row = (int)(e / nang), j = (int)(e % nang);
     const int ax = j / a.F, f = j % a.F;
-    const double phi = (double)a.pos[3 * (int64_t)row + ax] * a.inv_freq[f];
+    const double phi = ((double)a.pos[3 * (int64_t)row + ax] * a.pos_scale[ax]) * a.inv_freq[f];
     double sd, cd;
     sincos(phi, &sd, &cd);
     rope[e] = make_float2((float)cd, (float)sd);

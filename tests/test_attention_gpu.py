@@ -87,6 +87,26 @@ def test_attention_full_parity(case):
     assert np.allclose(r.lse_np(), lse, atol=2e-2, rtol=0), "lse"
 
 
+def test_attention_preview_grid_halved_spatial_rope():
+    """The engine page's 256x256 preview: an 8x8 spatial token grid whose h and
+    w RoPE coordinates are halved (pos_scale 1, 1/2, 1/2: half-integer
+    positions), through the whole attention path, against the oracle with the
+    same scale; the scale must change the result."""
+    rng = np.random.default_rng(40)
+    lay = synth.layout_from_counts(64, (9, 8, 8), 32, 40, T=1)
+    L, H = lay["L"], 4
+    q, k, v = (synth.normal_bf16(rng, (L, H, 128)) for _ in range(3))
+    inp = {"q": q, "k": k, "v": v, "layout": lay, "H": H, "D": 128}
+    sc = (1.0, 0.5, 0.5)
+    say(f"attention preview grid L={L} pos_scale={sc}")
+    r = AttentionRun(inp, pos_scale=sc).run()
+    ref, lse = oracle.attention_path(q, k, v, lay, H, pos_scale=sc)
+    assert_close(r.out(), ref, "preview halved")
+    assert np.allclose(r.lse_np(), lse, atol=2e-2, rtol=0), "lse"
+    plain, _ = oracle.attention_path(q, k, v, lay, H)
+    assert np.abs(plain - ref).max() > 0.05   # halving is visible in the output
+
+
 @pytest.mark.parametrize("name", ["nopad_L4096", "masked_L16384", "long_L32768"])
 def test_attention_workload_sampled_rows(name):
     wl = synth.workload(name)

@@ -158,8 +158,10 @@ def test_linear_epilogues_match_numpy(epi, M):
 _one_rounding = one_rounding
 
 
-@pytest.mark.parametrize("F,L,H,hidden", [(16, 700, 4, 512), (8, 300, 2, 256)])
-def test_qkv_projection_matches_oracle(F, L, H, hidden):
+@pytest.mark.parametrize("F,L,H,hidden,sc", [(16, 700, 4, 512, (1.0, 1.0, 1.0)),
+                                             (8, 300, 2, 256, (1.0, 1.0, 1.0)),
+                                             (16, 500, 2, 256, (1.0, 0.5, 0.5))])
+def test_qkv_projection_matches_oracle(F, L, H, hidden, sc):
     """pma_qkv_projection (QKV GEMM with the QK-norm + RoPE epilogue) against
     the oracle's norm and rotation of the fp64 product, and against the
     unfused GPU path (pma_linear + pma_qk_norm_rope) on the same inputs."""
@@ -178,7 +180,7 @@ def test_qkv_projection_matches_oracle(F, L, H, hidden):
     wk = rng.uniform(0.5, 2.0, 128).astype(np.float32)
     say(f"qkv projection F={F} L={L} H={H} hidden={hidden}")
     dl = B.pma_layout_build(lay)
-    p = B.attn_params(H, F=F)
+    p = B.attn_params(H, F=F, pos_scale=sc)
     Lp = B.pma_attention_padded_len(L)
     a, w = to_dev_bf16(a_bits), to_dev_bf16(w_bits)
     wq_d, wk_d = torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda()
@@ -198,7 +200,7 @@ def test_qkv_projection_matches_oracle(F, L, H, hidden):
 
     # rope table: fp32 rounding of the fp64 cos/sin of pos[i][a] * theta^(-f/F)
     inv = oracle.inv_freq(F, 10000.0)
-    phi = pos[:, :, None].astype(np.float64) * inv[None, None, :]       # [L, 3, F]
+    phi = (pos.astype(np.float64) * np.asarray(sc))[:, :, None] * inv[None, None, :]   # [L, 3, F]
     tab = rope.cpu().numpy().reshape(L, 3, F, 2)
     assert np.abs(tab[..., 0] - np.cos(phi)).max() <= 2.0 ** -24
     assert np.abs(tab[..., 1] - np.sin(phi)).max() <= 2.0 ** -24
@@ -206,7 +208,8 @@ def test_qkv_projection_matches_oracle(F, L, H, hidden):
     A64, W64 = oracle.bf16_to_f64(a_bits), oracle.bf16_to_f64(w_bits)
     q, k, v = (A64 @ W64[i * HD:(i + 1) * HD].T for i in range(3))
     for name, got_t, x, wv in (("q'", qh, q, wq), ("k'", kh, k, wk)):
-        ref = oracle.qk_norm_rope(x, H, 128, wv.astype(np.float64), pos, F=F).transpose(1, 0, 2)
+        ref = oracle.qk_norm_rope(x, H, 128, wv.astype(np.float64), pos, F=F,
+                                  pos_scale=sc).transpose(1, 0, 2)
         got = bf16_to_np(got_t)
         err = np.abs(got[:, :L] - ref)
         bad = err > _one_rounding(ref)
