@@ -142,6 +142,74 @@ def cpu_baseline(inp: dict, target_s: float = 12.0) -> dict:
                       f"took {t_prep:.1f} s and is not in the rate"}
 
 
+def block_cpu_baseline(inp: dict, target_s: float = 12.0) -> dict:
+    """The oracle's DiT block (numpy fp64 with bf16 storage, the fused-QKV
+    rounding) for a random sample of query rows.  It always projects K and V
+    of every row (attention needs them); the counted FLOPs are the work it
+    does: the K/V projection of all rows plus, per sampled row, the Q
+    projection, attention over the row's document, O-projection and FFN."""
+    import numpy as np
+    import oracle
+    from oracle import block as oblock
+    lay = inp["layout"]
+    L, hid, H, D, ffn = inp["L"], inp["hidden"], inp["heads"], inp["head_dim"], inp["ffn"]
+    HD = H * D
+    tags = np.asarray(lay["tags"])
+    pad = tags == -1
+    n_doc = np.where(pad, pad.sum(), (~pad).sum())
+    rng = np.random.default_rng(0)
+
+    def run(n):
+        rows = np.sort(rng.choice(L, size=n, replace=False))
+        t0 = time.perf_counter()
+        oblock.block_forward(inp, rows=rows, fused_qkv=True)
+        dt = time.perf_counter() - t0
+        fl = 2 * L * hid * 2 * HD + sum(2 * hid * HD + 4 * HD * int(n_doc[r]) + 2 * HD * hid
+                                         + 2 * hid * 2 * ffn + 2 * ffn * hid for r in rows)
+        return rows.size, dt, fl
+
+    n, dt, fl = run(16)
+    if dt < target_s / 2:
+        n, dt, fl = run(int(min(L, 16 * max(1.0, target_s / max(dt, 1e-3)))))
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 block for {n} random query rows of the L={L} workload ({dt:.1f} s), "
+                      f"including the K/V projection of all {L} rows the attention needs"}
+
+
+def io_cpu_baseline(d: dict, lay: dict, target_s: float = 10.0) -> dict:
+    """The oracle's input/output path (numpy fp64): timestep MLP and head table
+    in full, the video patch projection and video output head on a random
+    sample of video rows."""
+    import numpy as np
+    import oracle
+    from oracle import inout
+    t0 = time.perf_counter()
+    temb, _ = inout.timestep_mlp(d["t"].astype(np.float64), d["w1"], d["b1"], d["w2"], d["b2"],
+                                 freq_dim=d["freq_dim"])
+    table = inout.head_table(temb, d["w_mod"])
+    dt0 = time.perf_counter() - t0
+    T, hid, E, inner, fd = temb.shape[0], d["hidden"], d["temb_dim"], d["inner_dim"], d["freq_dim"]
+    fl0 = 2 * T * (fd * inner + inner * E) + 2 * T * E * 4 * hid
+    vidx = np.asarray(lay["video_idx"])
+    rng = np.random.default_rng(0)
+
+    def run(n):
+        pick = np.sort(rng.choice(vidx.size, size=min(n, vidx.size), replace=False))
+        t1 = time.perf_counter()
+        _ = d["video"][pick].astype(np.float64) @ d["w_video"].astype(np.float64).T + d["b_video"]
+        inout.output_head(d["x"], vidx[pick], lay["ts_idx"], table, 0, d["w_vout"], d["b_vout"])
+        return pick.size, time.perf_counter() - t1, 2 * pick.size * 96 * hid * 2
+
+    n, dt, fl = run(256)
+    if dt < target_s / 2:
+        n, dt, fl = run(int(256 * max(1.0, (target_s - dt0) / max(dt, 1e-3))))
+    return {"value": (fl0 + fl) / (dt0 + dt) / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"fp64 timestep MLP + head table ({dt0:.1f} s) and the video projection + "
+                      f"video head for {n} random video rows ({dt:.1f} s)"}
+
+
 def copy_probe(nbytes: int) -> None:
     """A plain device copy of known size, for scaling rocprofv3 HBM counters."""
     import torch
@@ -230,6 +298,9 @@ def block_bench(args) -> int:
                      "traffic": None, "avg_ms": round(fc1_ms, 4)},
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        outj["cpu_baseline"] = block_cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(outj), flush=True)
     return 0
 
@@ -330,6 +401,9 @@ def io_bench(args) -> int:
                      "traffic": None, "avg_ms": round(proj_ms, 4)},
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        outj["cpu_baseline"] = io_cpu_baseline(d, lay, args.cpu_seconds)
     print(json.dumps(outj), flush=True)
     return 0
 

@@ -27,7 +27,7 @@ _KEYS = ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
 @pytest.mark.gpu
 @pytest.mark.parametrize("args", [
     ["--steps", "2", "--warmup", "1", "--no-cpu-baseline"],
-    ["--workload", "block_L8192", "--steps", "2", "--warmup", "1"],
+    ["--workload", "block_L8192", "--steps", "2", "--warmup", "1", "--no-cpu-baseline"],
     ["--workload", "io_L8192", "--steps", "3", "--warmup", "1"],
 ])
 def test_bench_prints_one_complete_json_line(args):
