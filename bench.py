@@ -96,15 +96,17 @@ def attention_flops(tags, H: int, D: int) -> int:
     return 4 * H * D * (npad * npad + nreal * nreal)
 
 
-def traffic_from_profiles():
-    """HBM bytes per flash launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
-    if not os.path.exists(COUNTERS):
+def traffic_from_profiles(path: str = COUNTERS, source: str = "flash_fwd.hip",
+                          key: str = "flash_fwd_sha256_16"):
+    """HBM bytes per launch of a kernel from committed rocprofv3 counter runs
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size), if they were
+    taken on the current kernel source; else None."""
+    if not os.path.exists(path):
         return None
-    with open(COUNTERS) as fh:
+    with open(path) as fh:
         c = json.load(fh)
-    src = os.path.join(ROOT, "packed_masked_attention_amd", "csrc", "flash_fwd.hip")
-    if c.get("flash_fwd_sha256_16") != source_hash(src):
+    src = os.path.join(ROOT, "packed_masked_attention_amd", "csrc", source)
+    if c.get(key) != source_hash(src):
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -295,7 +297,10 @@ def block_bench(args) -> int:
         "roofline": {"kernel": "gemm_kernel<SWIGLU> (fc1)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "avg_ms": round(fc1_ms, 4)},
+                     "traffic": traffic_from_profiles(
+                         os.path.join(ROOT, "profiles", "gemm_fc1_block_L8192_counters.json"),
+                         "gemm.hip", "source_sha256_16"),
+                     "avg_ms": round(fc1_ms, 4)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -398,7 +403,10 @@ def io_bench(args) -> int:
         "roofline": {"kernel": "proj_scatter_kernel (video patch projection)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": FP32_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 4),
-                     "traffic": None, "avg_ms": round(proj_ms, 4)},
+                     "traffic": traffic_from_profiles(
+                         os.path.join(ROOT, "profiles", "proj_scatter_video_io_L8192_counters.json"),
+                         "inout.hip", "source_sha256_16"),
+                     "avg_ms": round(proj_ms, 4)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
