@@ -138,18 +138,33 @@ constexpr int kProjRows = 128;     // data rows per block (2 waves x 2 tiles of 
 constexpr int kProjCols = 128;     // output columns per block (2 waves x 2 tiles of 32)
 constexpr int kProjKc = 32;        // K per LDS chunk
 constexpr int kProjPitch = kProjKc + 1;
+constexpr int kProjOutPitch = kProjCols + 8;   // bf16 per staged output row (16-byte rows, 2-way banks)
+// operand tiles during the K loop, the bf16 output tile after it
+constexpr int kProjSmemFloats =
+    (2 * kProjRows * kProjPitch > kProjRows * kProjOutPitch / 2) ? 2 * kProjRows * kProjPitch
+                                                                 : kProjRows * kProjOutPitch / 2;
 
 // Wider tiles (128 x 256 per block) measured slower: fewer resident waves.
 __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void proj_scatter_kernel(ProjLaunch a) {
     constexpr int NTW = 2;             // column tiles of 32 per wave
     constexpr int kCols = kProjCols;
-    __shared__ float as[kProjRows * kProjPitch];
-    __shared__ float bs[kCols * kProjPitch];
+    __shared__ __align__(16) float smem[kProjSmemFloats];
     __shared__ int32_t dst[kProjRows];
+    float *as = smem, *bs = smem + kProjRows * kProjPitch;
+    static_assert(kCols == kProjRows, "the two operand tiles share one buffer");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int r0 = blockIdx.x * kProjRows, n0 = blockIdx.y * kCols;
+    // XCD-aware order: the dispatcher deals workgroups round-robin to the 8
+    // XCDs, so workgroup b takes item (b % 8) * per_xcd + b / 8; items run
+    // row tiles fastest, so an XCD sweeps a few column tiles (weights) over
+    // every row tile (inputs), both L2-resident
+    const int row_tiles = (a.rows + kProjRows - 1) / kProjRows;
+    const int total = row_tiles * (a.N / kCols);
+    const int per_xcd = (total + 7) / 8;
+    const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if (item >= total) return;
+    const int r0 = (item % row_tiles) * kProjRows, n0 = (item / row_tiles) * kCols;
     if (tid < kProjRows) {
         const int r = r0 + tid;
         int d = -1;
@@ -214,24 +229,36 @@ void proj_scatter_kernel(ProjLaunch a) {
     }
     // D register v of tile (i, j): output column 8(v/4) + 4(lane/32) + v%4 of
     // column tile j, data row lane%32 of row tile i -> 4 adjacent columns per
-    // group of 4 registers, stored as one 8-byte write
+    // group of 4 registers.  The bf16 tile goes through LDS so that every
+    // global store covers whole 128-byte lines (a partial line would make the
+    // L2 fetch the rest of it).
+    __syncthreads();   // every wave is done with the operand tiles
+    uint16_t *ot = reinterpret_cast<uint16_t *>(smem);   // [128 rows][kProjOutPitch]
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int d = dst[64 * wm + 32 * i + l32];
-        if (d < 0) continue;
-        uint16_t *orow = a.out + (int64_t)d * a.ld_out;
+        const int row = 64 * wm + 32 * i + l32;
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int col = n0 + 32 * NTW * wn + 32 * j + 8 * g + 4 * hk;
-                const f32x4 bias = *reinterpret_cast<const f32x4 *>(a.b + col);
+                const int c = 32 * NTW * wn + 32 * j + 8 * g + 4 * hk;
+                const f32x4 bias = *reinterpret_cast<const f32x4 *>(a.b + n0 + c);
                 uint2 w;
                 w.x = pack_bf16x2(acc[i][j][4 * g] + bias[0], acc[i][j][4 * g + 1] + bias[1]);
                 w.y = pack_bf16x2(acc[i][j][4 * g + 2] + bias[2], acc[i][j][4 * g + 3] + bias[3]);
-                *reinterpret_cast<uint2 *>(orow + col) = w;
+                *reinterpret_cast<uint2 *>(ot + row * kProjOutPitch + c) = w;
             }
         }
+    }
+    __syncthreads();
+    // 16 threads per 256-byte row segment, 16 rows per pass
+#pragma unroll
+    for (int it = 0; it < kProjRows / 16; ++it) {
+        const int row = it * 16 + (tid >> 4), ch = tid & 15;
+        const int d = dst[row];
+        if (d >= 0)
+            *reinterpret_cast<uint4 *>(a.out + (int64_t)d * a.ld_out + n0 + 8 * ch) =
+                *reinterpret_cast<const uint4 *>(ot + row * kProjOutPitch + 8 * ch);
     }
 }
 
@@ -424,8 +451,8 @@ int gemv_max_t() { return kGemvMaxT; }
 
 hipError_t launch_proj_scatter(const ProjLaunch &a, hipStream_t s) {
     if (a.rows == 0) return hipSuccess;
-    dim3 grid((a.rows + kProjRows - 1) / kProjRows, a.N / kProjCols);
-    proj_scatter_kernel<<<grid, kProjThreads, 0, s>>>(a);
+    const int total = ((a.rows + kProjRows - 1) / kProjRows) * (a.N / kProjCols);
+    proj_scatter_kernel<<<8 * ((total + 7) / 8), kProjThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 
