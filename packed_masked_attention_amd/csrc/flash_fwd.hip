@@ -27,14 +27,18 @@
 //  * Softmax in fp32 with exp2 (log2 e folded into the scale) and a lazy
 //    reference max: a row's reference only moves when its max grows by more
 //    than 2^8 (so p <= 256), which makes the O rescale rare.  The row max is
-//    four independent max3 chains and the row sum four independent add
-//    chains: the softmax wave has no other wave to hide its latencies behind.
+//    four independent chains of three-input IEEE maximum (NaN-propagating,
+//    so the raw MFMA results need no canonicalising first) and the row sum
+//    four independent add chains: the softmax wave has no other wave to hide
+//    its latencies behind.
 //  * K, V^T tiles (64 keys) stream through a 4-deep LDS ring filled by
 //    direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds) with the tile
 //    offset in an SGPR.  Every wave issues its share of tile t+3's K and
-//    t+2's V^T at the start of its G(t); phase ends wait for all but the
-//    newest one or two batches, so each batch has three phases to land and
-//    no wave waits for a tile it just requested.  The 64 document ids of a V
+//    t+2's V^T during its G(t), one instruction every few MFMAs (issued in
+//    a burst at the phase start, the instructions of the four waves queue
+//    behind each other and hold back the first MFMAs); phase ends wait for
+//    all but the newest one or two batches, so each batch has about three
+//    phases to land and no wave waits for a tile it just requested.  The 64 document ids of a V
 //    tile's keys ride along in the same slot (for the rare masked tile).
 //    Each 1 KB wave-instruction fills LDS in lane order, so instead of row
 //    padding the 16-byte chunks of a row are XOR-swizzled (chosen by the
@@ -69,6 +73,7 @@ constexpr int kMask = 0x3fffffff;          // list entry -> k-tile index
 constexpr int kStaticLds = 4 * kTileElems * 2 + 4 * (kTileElems + 2 * kBN) * 2;
 constexpr int kLdsBytes = 160 * 1024;      // per workgroup on gfx950
 static_assert(kKI * kNW == 16, "16 KB tiles split over the waves");
+static_assert(kKI == 2, "the MFMA phase spreads two K and two V^T DMA instructions per wave");
 
 // LDS placement of 16-byte chunk c of a tile row:
 //   K tile   [64 keys][16 chunks]: position c ^ (row & 15)
@@ -112,7 +117,7 @@ __device__ __forceinline__ int k_slab_row(int i) {
 __device__ __forceinline__ float half_max(float x) {
     const uint32_t u = __float_as_uint(x);
     const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float half_sum(float x) {
     const uint32_t u = __float_as_uint(x);
@@ -211,17 +216,25 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch a) {
         vvo[i] = 2u * ((uint32_t)vr * (uint32_t)a.Lp + 8u * v_pos(vr, vp));
     }
     const uint32_t dvo = 4u * (uint32_t)(wave * 8 + (lane & 7));
+    // wave-instruction i of this wave's share of a K or V^T tile, and the
+    // document ids of a V tile's keys (8 per wave: lanes 0..7)
+    auto dma_k1 = [&](int kt, uint16_t *dst, int i) __attribute__((always_inline)) {
+        dma16(krs, (lds_void *)&dst[(wave * kKI + i) * 512], kvo[i], (uint32_t)kt * (kBN * kD * 2));
+    };
+    auto dma_v1 = [&](int kt, uint16_t *dst, int i) __attribute__((always_inline)) {
+        dma16(vrs, (lds_void *)&dst[(wave * kKI + i) * 512], vvo[i], (uint32_t)kt * (kBN * 2));
+    };
+    auto dma_id = [&](int kt, uint16_t *dst) __attribute__((always_inline)) {
+        if (lane < 8) dma4(drs, (lds_void *)&dst[kTileElems + wave * 16], dvo, (uint32_t)kt * (kBN * 4));
+    };
     auto dma_k = [&](int kt, uint16_t *dst) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < kKI; ++i)
-            dma16(krs, (lds_void *)&dst[(wave * kKI + i) * 512], kvo[i], (uint32_t)kt * (kBN * kD * 2));
+        for (int i = 0; i < kKI; ++i) dma_k1(kt, dst, i);
     };
-    // V^T tile plus the document ids of its keys (8 per wave: lanes 0..7)
     auto dma_v = [&](int kt, uint16_t *dst) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < kKI; ++i)
-            dma16(vrs, (lds_void *)&dst[(wave * kKI + i) * 512], vvo[i], (uint32_t)kt * (kBN * 2));
-        if (lane < 8) dma4(drs, (lds_void *)&dst[kTileElems + wave * 16], dvo, (uint32_t)kt * (kBN * 4));
+        for (int i = 0; i < kKI; ++i) dma_v1(kt, dst, i);
+        dma_id(kt, dst);
     };
 
     const int krow = k_slab_row(l32);
@@ -239,8 +252,18 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch a) {
     bf16x8 vpre[kVPre];
 
     // ---- MFMA phase: O^T += V(t-1)^T P(t-1)^T (when withpv), S(t) = K(t) Q^T
-    auto gphase = [&](bool withpv, const uint16_t *vr, const uint16_t *kr) __attribute__((always_inline)) {
+    auto gphase = [&](bool withpv, const uint16_t *vr, const uint16_t *kr, int dk, uint16_t *dks,
+                      int dv, uint16_t *dvs) __attribute__((always_inline)) {
+        // the document-id DMA (8 lanes) ahead of the scheduled region: its
+        // lane branch would split the MFMA block
+        dma_id(dv, dvs);
         __builtin_amdgcn_s_setprio(1);
+        if (!withpv) {
+            // the first tile has no PV half to spread them over
+            dma_k(dk, dks);
+#pragma unroll
+            for (int i = 0; i < kKI; ++i) dma_v1(dv, dvs, i);
+        }
         if (withpv) {
             // channel blocks interleaved so consecutive MFMAs are independent
 #pragma unroll
@@ -252,6 +275,11 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch a) {
                     const bf16x8 vf = f < kVPre ? vpre[f < kVPre ? f : 0]
                                                 : *reinterpret_cast<const bf16x8 *>(vr + d * kBN + 8 * v_pos(d, 2 * cc + hi));
                     o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[cc], o[db], 0, 0, 0);
+                    // this wave's share of the ring refill, spread over the
+                    // phase rather than issued in one burst (kKI == 2)
+                    if (f == 2) dma_k1(dk, dks, 0);
+                    if (f == 8) dma_k1(dk, dks, 1);
+                    if (f == 14) dma_v1(dv, dvs, 0);
                 }
         }
 #pragma unroll
@@ -265,13 +293,17 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch a) {
                 const int r = 32 * kb + krow;
                 const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kr + r * kD + 8 * k_pos(r, 2 * c + hi));
                 s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
+                if (withpv && c == 2 && kb == 1) dma_v1(dv, dvs, 1);
             }
-        // LDS fragment reads run kReadAhead ahead of their MFMAs
+        // LDS fragment reads run kReadAhead ahead of their MFMAs; the DMA
+        // instructions sit between MFMAs
         __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (i == 2 || i == 8 || i == 14 || i == 21)
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
         __builtin_amdgcn_s_setprio(0);
     };
@@ -308,28 +340,32 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch a) {
                 for (int v = 0; v < 16; ++v)
                     if (!((m32 >> (16 * kb + v)) & 1u)) s[kb][v] = -INFINITY;
         }
-        // row max over four independent max3 chains (the three-input form
-        // takes the raw MFMA results; a tree of two-input maxima would first
-        // canonicalize every leaf)
+        // row max over four independent chains of IEEE maximum, which the
+        // compiler fuses into three-input v_maximum3 on the raw MFMA results
+        // (fmaxf would canonicalise every input first)
         float m4[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int b = 8 * (g & 1);
-            float m = fmaxf(s[g >> 1][b], s[g >> 1][b + 1]);
+            float m = __builtin_elementwise_maximum(s[g >> 1][b], s[g >> 1][b + 1]);
 #pragma unroll
-            for (int k = 2; k < 8; k += 2) m = fmaxf(fmaxf(m, s[g >> 1][b + k]), s[g >> 1][b + k + 1]);
+            for (int k = 2; k < 8; k += 2)
+                m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, s[g >> 1][b + k]),
+                                                  s[g >> 1][b + k + 1]);
             m4[g] = m;
         }
-        float mx = fmaxf(fmaxf(fmaxf(m4[0], m4[1]), m4[2]), m4[3]);
+        float mx = __builtin_elementwise_maximum(
+            __builtin_elementwise_maximum(__builtin_elementwise_maximum(m4[0], m4[1]), m4[2]), m4[3]);
         mx = half_max(mx) * c2;
         const bool need = mx > mref + 8.0f;
         const float mnew = need ? mx : mref;
         const float alpha = need ? __builtin_amdgcn_exp2f(mref - mnew) : 1.0f;
         mref = mnew;
         const float mu = (mnew == -INFINITY) ? 0.f : mnew;
-        // probabilities; the row sum (four independent chains) is taken over
-        // the fp32 values before their rounding to bf16
-        float rsp[4] = {0.f, 0.f, 0.f, 0.f};
+        // probabilities; the row sum (four independent chains, each started
+        // by its first pair rather than by adding to zero) is taken over the
+        // fp32 values before their rounding to bf16
+        float rsp[4];
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
             bf16x2 pp[4];
@@ -339,7 +375,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch a) {
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(s[cc >> 1][8 * (cc & 1) + 2 * t + 1], c2, -mu));
                 const f32x2 pv = {p0, p1};
                 pp[t] = __builtin_convertvector(pv, bf16x2);
-                rsp[t] += p0 + p1;
+                rsp[t] = cc ? rsp[t] + (p0 + p1) : p0 + p1;
             }
             pf[cc] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
                                              __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
@@ -366,8 +402,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch a) {
     // Global phase p: group 0 runs G(t) at p = 2t and S(t) at 2t + 1; group 1
     // runs one phase later.  Tile x sits in ring slot x % 4.  K(t) is read in
     // phases 2t, 2t+1; V(t) in 2t+1 .. 2t+3.  Each wave issues its share of
-    // DMA(t) = {K(t+3), V(t+2)} at the start of its G(t) (the slots of K(t-1)
-    // and V(t-2), both done with by the end of phase 2t-1); the waits at
+    // DMA(t) = {K(t+3), V(t+2)} during its G(t) (the slots of K(t-1) and
+    // V(t-2), both done with by the end of phase 2t-1); the waits at
     // phase ends (two batches may stay in flight after G, one after S) make
     // DMA(t) land by the end of phase 2t+4, before either tile is first read.
     if (grp == 1) PMA_PHASE_END(0);
@@ -384,9 +420,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch a) {
     auto tile = [&](int t, bool withpv, uint16_t *k_r, uint16_t *k_m, uint16_t *v_r,
                     uint16_t *v_p, uint16_t *v_q) __attribute__((always_inline)) {
         const int e = ce;
-        dma_k(ck & kMask, k_m);
-        dma_v(cv & kMask, v_q);
-        gphase(withpv, v_p, k_r);
+        gphase(withpv, v_p, k_r, ck & kMask, k_m, cv & kMask, v_q);
         PMA_PHASE_END(2 * kNDMA);
         const int ne = tlist[t + 1], nk = tlist[t + 4], nv = tlist[t + 3];
         sphase(e, v_r);
