@@ -193,6 +193,11 @@ pma_status pma_qk_norm_rope(const pma_attn_params *p, const pma_layout *layout,
                             const float *q_norm_weight, const float *k_norm_weight,
                             pma_bf16 *qh, pma_bf16 *kh, pma_bf16 *vt, void *stream);
 
+/* Bytes of the optional workspace of pma_flash_attention: 256 bytes of
+ * work-queue counters, then the partial results of the items whose key
+ * ranges are split (none below 12288 keys). */
+pma_status pma_flash_workspace_size(const pma_attn_params *p, int32_t seq_len, size_t *bytes);
+
 /* Masked flash attention forward on the operands of pma_qk_norm_rope.
  * layout must be built with pma_attention_tiles()' tiling.  Tiles the layout
  * marks EMPTY are skipped whole; PARTIAL tiles and the ragged last k-tile
@@ -200,13 +205,25 @@ pma_status pma_qk_norm_rope(const pma_attn_params *p, const pma_layout *layout,
  *   o:   bf16 token-major, row i of head h at o[i*o_ld + h*D .. + D), o_ld >= H*D,
  *        o_ld % 8 == 0.  Only rows < L are written.
  *   lse: fp32 [H][L] natural-log sum of exp of the scaled logits (NULL: not written).
+ *   workspace: NULL, or >= pma_flash_workspace_size() bytes, 256-byte aligned,
+ *        owned by the caller and overwritten (contents need no clearing).
+ *        From 12288 keys on, it holds a work queue: one workgroup per CU
+ *        pulls (head, q-tile) items, first its own XCD's then what is left of
+ *        the others', and the last items of every XCD's share run as four
+ *        parts over their key ranges, whose partial softmax results a second
+ *        kernel merges.  Shorter sequences, or NULL, run one item per
+ *        workgroup.  The two agree to fp32 rounding order (each part rounds
+ *        its probabilities to bf16 against its own running maximum).
+ *        Calls that share one workspace must not overlap.
  * The kernel keeps each q-tile's k-tile list in LDS: layouts of more than
  * 7932 k-tiles (seq_len > 507648) return PMA_ERR_SHAPE. */
 pma_status pma_flash_attention(const pma_attn_params *p, const pma_layout *layout,
                                const pma_bf16 *qh, const pma_bf16 *kh, const pma_bf16 *vt,
-                               pma_bf16 *o, int64_t o_ld, float *lse, void *stream);
+                               pma_bf16 *o, int64_t o_ld, float *lse, void *workspace,
+                               size_t workspace_bytes, void *stream);
 
-/* Workspace of pma_attention: qh, kh and vt (3 * H * Lp * D bf16). */
+/* Workspace of pma_attention: qh, kh and vt (3 * H * Lp * D bf16), then the
+ * flash workspace (pma_flash_workspace_size). */
 pma_status pma_attention_workspace_size(const pma_attn_params *p, int32_t seq_len,
                                         size_t *bytes);
 

@@ -97,8 +97,10 @@ _SIGS = {
     "pma_attention_padded_len": (_i32, [_i32, ctypes.POINTER(_i32)]),
     "pma_qk_norm_rope": (_i32, [ctypes.POINTER(AttnParams), ctypes.POINTER(Layout), _vp, _i64, _vp,
                                 _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "pma_flash_workspace_size": (_i32, [ctypes.POINTER(AttnParams), _i32,
+                                        ctypes.POINTER(ctypes.c_size_t)]),
     "pma_flash_attention": (_i32, [ctypes.POINTER(AttnParams), ctypes.POINTER(Layout), _vp, _vp,
-                                   _vp, _vp, _i64, _vp, _vp]),
+                                   _vp, _vp, _i64, _vp, _vp, ctypes.c_size_t, _vp]),
     "pma_attention_workspace_size": (_i32, [ctypes.POINTER(AttnParams), _i32,
                                             ctypes.POINTER(ctypes.c_size_t)]),
     "pma_attention": (_i32, [ctypes.POINTER(AttnParams), ctypes.POINTER(Layout), _vp, _i64, _vp,
@@ -301,10 +303,20 @@ def pma_qkv_projection(p: AttnParams, dl: DeviceLayout, a, lda, hidden, w_qkv, w
                                    ptr(vt), stream_ptr(stream)))
 
 
+def pma_flash_workspace_size(p: AttnParams, seq_len: int) -> int:
+    n = ctypes.c_size_t()
+    check(lib().pma_flash_workspace_size(ctypes.byref(p), seq_len, ctypes.byref(n)))
+    return n.value
+
+
 def pma_flash_attention(p: AttnParams, dl: DeviceLayout, qh, kh, vt, o, o_ld, lse=None,
-                        stream=None) -> None:
+                        workspace=None, stream=None) -> None:
+    """workspace: None (every item whole) or a device buffer of at least
+    pma_flash_workspace_size bytes (the last items split over their keys)."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(lib().pma_flash_attention(ctypes.byref(p), ctypes.byref(dl.struct), ptr(qh), ptr(kh),
-                                    ptr(vt), ptr(o), o_ld, ptr(lse), stream_ptr(stream)))
+                                    ptr(vt), ptr(o), o_ld, ptr(lse), ptr(workspace), nbytes,
+                                    stream_ptr(stream)))
 
 
 def pma_attention_workspace_size(p: AttnParams, seq_len: int) -> int:

@@ -298,9 +298,19 @@ pma_status pma_qk_norm_rope(const pma_attn_params *p, const pma_layout *layout,
     return PMA_OK;
 }
 
+pma_status pma_flash_workspace_size(const pma_attn_params *p, int32_t seq_len, size_t *bytes) {
+    pma_status st;
+    if ((st = check_attn_params(p)) != PMA_OK) return st;
+    if (!bytes) return fail(PMA_ERR_NULL, "bytes is NULL");
+    if (seq_len < 1 || seq_len > (1 << 24)) return fail(PMA_ERR_SHAPE, "seq_len %d", seq_len);
+    *bytes = flash_split_bytes(p->num_heads, seq_len);
+    return PMA_OK;
+}
+
 pma_status pma_flash_attention(const pma_attn_params *p, const pma_layout *layout,
                                const pma_bf16 *qh, const pma_bf16 *kh, const pma_bf16 *vt,
-                               pma_bf16 *o, int64_t o_ld, float *lse, void *stream) {
+                               pma_bf16 *o, int64_t o_ld, float *lse, void *workspace,
+                               size_t workspace_bytes, void *stream) {
     pma_status st;
     if ((st = check_attn_params(p)) != PMA_OK) return st;
     if ((st = check_layout(layout)) != PMA_OK) return st;
@@ -317,6 +327,13 @@ pma_status pma_flash_attention(const pma_attn_params *p, const pma_layout *layou
         return fail(PMA_ERR_ALIGN, "qh, kh, vt must be 16-byte aligned");
     if ((st = check_tok_major("o", o, o_ld, p->num_heads)) != PMA_OK) return st;
     if (lse && !aligned(lse, 4)) return fail(PMA_ERR_ALIGN, "lse must be 4-byte aligned");
+    if (workspace) {
+        size_t need = 0;
+        if ((st = pma_flash_workspace_size(p, layout->seq_len, &need)) != PMA_OK) return st;
+        if (!aligned(workspace, 256)) return fail(PMA_ERR_ALIGN, "workspace must be 256-byte aligned");
+        if (workspace_bytes < need)
+            return fail(PMA_ERR_WORKSPACE, "flash workspace %zu < %zu bytes", workspace_bytes, need);
+    }
     if ((st = check_device()) != PMA_OK) return st;
 
     const float scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)kHeadDim);
@@ -335,6 +352,12 @@ pma_status pma_flash_attention(const pma_attn_params *p, const pma_layout *layou
     a.count = layout->tile_count;
     a.list = layout->tile_list;
     a.order = layout->tile_order;
+    // the work queue pays off on long key lists only (see flash_split_items)
+    a.split_items = workspace ? flash_split_items(a.H, a.L) : 0;
+    a.queue = a.split_items > 0 ? static_cast<int32_t *>(workspace) : nullptr;
+    a.part = a.split_items > 0
+                 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + kFlashQueueBytes)
+                 : nullptr;
     PMA_CHECK_HIP(launch_flash_attention(a, static_cast<hipStream_t>(stream)), "flash launch");
     return PMA_OK;
 }
@@ -346,7 +369,9 @@ pma_status pma_attention_workspace_size(const pma_attn_params *p, int32_t seq_le
     if (!bytes) return fail(PMA_ERR_NULL, "bytes is NULL");
     if (seq_len < 1 || seq_len > (1 << 24)) return fail(PMA_ERR_SHAPE, "seq_len %d", seq_len);
     const size_t one = round_up((size_t)p->num_heads * padded_len(seq_len) * kHeadDim * 2, 256);
-    *bytes = 3 * one;
+    size_t flash = 0;
+    if ((st = pma_flash_workspace_size(p, seq_len, &flash)) != PMA_OK) return st;
+    *bytes = 3 * one + flash;
     return PMA_OK;
 }
 
@@ -363,14 +388,15 @@ pma_status pma_attention(const pma_attn_params *p, const pma_layout *layout, con
     if (!aligned(workspace, 256)) return fail(PMA_ERR_ALIGN, "workspace must be 256-byte aligned");
     if (workspace_bytes < need)
         return fail(PMA_ERR_WORKSPACE, "attention workspace %zu < %zu bytes", workspace_bytes, need);
-    const size_t one = need / 3;
+    const size_t one = round_up((size_t)p->num_heads * padded_len(layout->seq_len) * kHeadDim * 2, 256);
     pma_bf16 *qh = static_cast<pma_bf16 *>(workspace);
     pma_bf16 *kh = reinterpret_cast<pma_bf16 *>(static_cast<char *>(workspace) + one);
     pma_bf16 *vt = reinterpret_cast<pma_bf16 *>(static_cast<char *>(workspace) + 2 * one);
     if ((st = pma_qk_norm_rope(p, layout, q, q_ld, k, k_ld, v, v_ld, q_norm_weight, k_norm_weight,
                                qh, kh, vt, stream)) != PMA_OK)
         return st;
-    return pma_flash_attention(p, layout, qh, kh, vt, o, o_ld, lse, stream);
+    return pma_flash_attention(p, layout, qh, kh, vt, o, o_ld, lse,
+                               static_cast<char *>(workspace) + 3 * one, need - 3 * one, stream);
 }
 
 }  // extern "C"

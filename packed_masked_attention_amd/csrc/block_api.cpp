@@ -265,7 +265,9 @@ pma_status block_forward_impl(const pma_block_params *p, const pma_layout *layou
     if ((st = pma_qkv_projection(&p->attn, layout, ab, hid, hid, w->w_qkv, w->q_norm_weight,
                                  w->k_norm_weight, rope, qh, kh, vt, stream)) != PMA_OK)
         return st;
-    if ((st = pma_flash_attention(&p->attn, layout, qh, kh, vt, o, HD, nullptr, stream)) != PMA_OK)
+    if ((st = pma_flash_attention(&p->attn, layout, qh, kh, vt, o, HD, nullptr,
+                                  static_cast<char *>(attn_ws) + 3 * one, attn_bytes - 3 * one,
+                                  stream)) != PMA_OK)
         return st;
     pma_linear_args g;
     // x1 = x + gate_a (O W_o^T)

@@ -52,6 +52,19 @@
 //    to the 8 XCDs, so workgroup b runs item (b % 8) * per_xcd + b / 8 and
 //    each XCD sweeps whole heads, keeping that head's K/V in its own L2.
 //    Within a head, q-tiles run heaviest first (the layout's order list).
+//  * Load balance (with a work-queue buffer): one workgroup per CU stays
+//    resident and pulls work units from atomic counters -- its own XCD's
+//    items first, then what is left of the other XCDs' shares.  The hardware
+//    deals workgroups to the XCDs, and within an XCD to its shader engines,
+//    in a fixed round-robin order, so with one item per workgroup a CU can
+//    wait for its turn while items of unequal cost (a masked layout's light
+//    padding q-tiles) and XCDs of unequal speed (on MI355X up to 10% apart
+//    on the same items) leave others idle.  The last units are parts: the
+//    last kSplitItems items of every XCD's share, each split over
+//    consecutive quarters of its key list, so the final units are short.  A
+//    part writes its unnormalised O, reference max and row sum, and
+//    flash_merge_kernel combines the parts (the split form of the online
+//    softmax: weights 2^(m_p - m) on each part's O and row sum).
 #include "internal.h"
 
 #include <cmath>
@@ -69,6 +82,12 @@ constexpr int kNDMA = 2 * kKI + 1;         // DMA instructions per wave per tile
 constexpr int kReadAhead = 4;              // LDS fragment reads in flight ahead of the MFMAs
 constexpr int kVPre = 4;                   // V fragments read during the softmax phase
 constexpr int kMask = 0x3fffffff;          // list entry -> k-tile index
+constexpr int kSplitItems = 16;            // items per XCD split over their key range
+constexpr int kSplitMinKeyTiles = 192;     // no split below this many k-tiles (12288 keys)
+constexpr int kSplitParts = 4;             // workgroups per split item
+// one part's partial result: O [kBM rows][kD] fp32, then (m, l) per row
+constexpr int kPartFloats = kBM * kD + 2 * kBM;
+static_assert(kFlashQueueBytes >= 16 * sizeof(int32_t), "the queue reset clears 16 counters");
 // LDS: 4 K slots + 4 V^T slots (each + 64 document ids) + the tile list
 constexpr int kStaticLds = 4 * kTileElems * 2 + 4 * (kTileElems + 2 * kBN) * 2;
 constexpr int kLdsBytes = 160 * 1024;      // per workgroup on gfx950
@@ -138,7 +157,45 @@ __device__ __forceinline__ float half_sum(float x) {
         asm volatile("s_barrier" ::: "memory");                                            \
     } while (0)
 
-__global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch a) {
+// The next unit of work of a workgroup: {item, part} (part -1: the whole
+// item; item -1: none left).  Without a work queue workgroup b takes item
+// (b % 8) * per_xcd + b / 8 and nothing more: the dispatcher deals
+// workgroups round-robin to the 8 XCDs, so each XCD sweeps whole heads.  With
+// one, the workgroups persist (one per CU) and pull units until none is left:
+// first the items of their own XCD's share (local indices [0, per_xcd - S),
+// in order, so its heads' K/V stay in its L2), then the remaining items of
+// the other XCDs' shares (neighbours first), then the kSplitParts parts of
+// the last S items of every share.  An XCD that runs ahead takes over the
+// tail of a slower one's share.
+__device__ __forceinline__ int2 next_work(const FlashLaunch &a, int xcd, int iter) {
+    const int total = a.H * a.nqt;
+    const int per_xcd = (total + 7) / 8;
+    if (!a.queue) {
+        const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+        return make_int2(iter == 0 && item < total ? item : -1, -1);
+    }
+    const int S = a.split_items;
+    for (int k = 0; k < 8; ++k) {
+        const int y = (xcd + k) & 7;
+        const int own = min(per_xcd - S, max(0, total - y * per_xcd));
+        // skip a share that is already handed out without touching its counter
+        if (k > 0 && __hip_atomic_load(&a.queue[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= own)
+            continue;
+        const int w = atomicAdd(&a.queue[y], 1);
+        if (w < own) return make_int2(y * per_xcd + w, -1);
+    }
+    for (;;) {
+        const int g = atomicAdd(&a.queue[8], 1);
+        if (g >= 8 * S * kSplitParts) return make_int2(-1, -1);
+        const int x = g / (S * kSplitParts), sp = g % (S * kSplitParts);
+        const int item = x * per_xcd + per_xcd - S + sp / kSplitParts;
+        if (item < total) return make_int2(item, sp % kSplitParts);
+    }
+}
+
+typedef __attribute__((address_space(4))) const FlashLaunch *kernarg_launch;
+
+__global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg) {
     // ring slots as distinct objects, so the compiler can tell the slot being
     // streamed into from the ones being read
     __shared__ __attribute__((aligned(1024))) uint16_t ks0[kTileElems];
@@ -163,16 +220,45 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch a) {
     const int grp = wave >> 2;
     const int l32 = lane & 31, hi = lane >> 5;
 
-    // ---- work item (XCD-aware)
+    // the XCD this workgroup runs on (hardware register XCC_ID)
+    const int xcd_hw = (int)(__builtin_amdgcn_s_getreg(20 | (15 << 11)) & 7);
+    __shared__ int2 work;
+    (void)arg;   // read through the kernarg segment below
+    for (int iter = 0;; ++iter) {
+    // the launch arguments, read again for every item, so that none of them
+    // stays live across the work loop
+    kernarg_launch ap = (kernarg_launch)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(ap));
+    FlashLaunch a;
+    __builtin_memcpy(&a, ap, sizeof(FlashLaunch));
+    if (tid == 0) work = next_work(a, xcd_hw, iter);
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(work.x);
+    const int part = __builtin_amdgcn_readfirstlane(work.y);
+    __syncthreads();   // every wave has read `work` before it is written again
+    if (item < 0) break;
     const int total = a.H * a.nqt;
     const int per_xcd = (total + 7) / 8;
-    const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-    if (item >= total) return;
     const int head = item / a.nqt;
     const int qt = a.order[item % a.nqt];
-    const int cnt = a.count[qt];
+    const int full = a.count[qt];
+    const int beg = part < 0 ? 0 : part * full / kSplitParts;
+    const int cnt = part < 0 ? full : (part + 1) * full / kSplitParts - beg;
+    // a part's partial result: slot of (owning XCD, split item, part)
+    const int owner = item / per_xcd, sidx = item % per_xcd - (per_xcd - a.split_items);
+    float *pres = part < 0 ? nullptr
+                           : a.part + (int64_t)((owner * a.split_items + sidx) * kSplitParts + part) *
+                                          kPartFloats;
+    if (cnt == 0) {
+        // an empty key range: a part with no weight
+        if (tid < kBM) {
+            pres[kBM * kD + 2 * tid] = -INFINITY;
+            pres[kBM * kD + 2 * tid + 1] = 0.f;
+        }
+        continue;
+    }
     {
-        const int32_t *list = a.list + (int64_t)qt * a.nkt;
+        const int32_t *list = a.list + (int64_t)qt * a.nkt + beg;
         const uint8_t *cls = a.cls + (int64_t)qt * a.nkt;
         for (int i = tid; i < cnt; i += kNW * 64) {
             const int kt = list[i];
@@ -468,6 +554,23 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch a) {
     // ---- epilogue: O row = O^T column / row sum; register v of d-block db is
     // channel 32*db + 8*(v/4) + 4*hi + v%4
     const float lt = half_sum(lsum);
+    if (part >= 0) {
+        // a part: unnormalised O (reference mref) and the row sum, for the merge
+        const int r = wave * 32 + l32;
+        float *orow = pres + r * kD + 4 * hi;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 w = {o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+                *reinterpret_cast<f32x4 *>(orow + 32 * db + 8 * g) = w;
+            }
+        if (hi == 0) {
+            pres[kBM * kD + 2 * r] = mref;
+            pres[kBM * kD + 2 * r + 1] = lt;
+        }
+        continue;
+    }
     const float inv = 1.0f / lt;
     if (qrow < a.L) {
         uint16_t *orow = a.o + (int64_t)qrow * a.o_ld + head * kD + 4 * hi;
@@ -483,9 +586,73 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch a) {
         if (a.lse && hi == 0)
             a.lse[(int64_t)head * a.L + qrow] = (mref + __log2f(lt)) * 0.69314718055994531f;
     }
+    }   // work loop
+}
+
+// Zero the work-queue counters (a kernel rather than a memset, so the
+// sequence can be captured in a graph and replayed).
+__global__ void flash_queue_reset_kernel(int *queue) {
+    if (threadIdx.x < 16) queue[threadIdx.x] = 0;
+}
+
+// Combine the parts of the split items: per row, m = max_p m_p and
+// O = sum_p 2^(m_p - m) O_p / sum_p 2^(m_p - m) l_p (parts with l_p = 0 hold
+// no key of the row's document and carry no weight).  One workgroup per
+// split item and 8 rows; 32 threads per row, 4 channels each.
+__global__ __launch_bounds__(256) void flash_merge_kernel(FlashLaunch a) {
+    const int total = a.H * a.nqt;
+    const int per_xcd = (total + 7) / 8;
+    const int gi = (int)blockIdx.x / (kBM / 8), rb = (int)blockIdx.x % (kBM / 8);
+    const int xcd = gi / a.split_items, s = gi % a.split_items;
+    const int item = xcd * per_xcd + per_xcd - a.split_items + s;
+    if (item >= total) return;
+    const int head = item / a.nqt;
+    const int qt = a.order[item % a.nqt];
+    const int r = rb * 8 + (int)(threadIdx.x >> 5), c4 = (int)(threadIdx.x & 31);
+    const int qrow = qt * kBM + r;
+    if (qrow >= a.L) return;
+    const float *base = a.part + (int64_t)gi * kSplitParts * kPartFloats;
+    float mp[kSplitParts], lp[kSplitParts], m = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < kSplitParts; ++p) {
+        mp[p] = base[p * kPartFloats + kBM * kD + 2 * r];
+        lp[p] = base[p * kPartFloats + kBM * kD + 2 * r + 1];
+        if (lp[p] > 0.f) m = fmaxf(m, mp[p]);
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+#pragma unroll
+    for (int p = 0; p < kSplitParts; ++p) {
+        if (!(lp[p] > 0.f)) continue;
+        const float w = __builtin_amdgcn_exp2f(mp[p] - m);
+        l = fmaf(w, lp[p], l);
+        const f32x4 op = *reinterpret_cast<const f32x4 *>(base + p * kPartFloats + r * kD + 4 * c4);
+        acc += w * op;
+    }
+    const float inv = 1.0f / l;
+    uint2 wv;
+    wv.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    wv.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<uint2 *>(a.o + (int64_t)qrow * a.o_ld + head * kD + 4 * c4) = wv;
+    if (a.lse && c4 == 0)
+        a.lse[(int64_t)head * a.L + qrow] = (m + __log2f(l)) * 0.69314718055994531f;
 }
 
 }  // namespace
+
+int32_t flash_split_items(int32_t H, int32_t L) {
+    // below kSplitMinKeyTiles an item is short enough that the queue's fetch
+    // and the parts' set-up cost more than the balance gains (measured: 4%
+    // slower at 4096 keys, 2-4% faster from 16384); 0 turns the queue off
+    const int nqt = (L + kBM - 1) / kBM, nkt = (L + kBN - 1) / kBN;
+    if (nkt < kSplitMinKeyTiles) return 0;
+    const int per_xcd = (H * nqt + 7) / 8;
+    return per_xcd < kSplitItems ? per_xcd : kSplitItems;
+}
+
+size_t flash_split_bytes(int32_t H, int32_t L) {
+    return kFlashQueueBytes + (size_t)8 * flash_split_items(H, L) * kSplitParts * kPartFloats * sizeof(float);
+}
 
 void flash_tiles(int32_t *tile_m, int32_t *tile_n) {
     *tile_m = kBM;
@@ -498,7 +665,18 @@ hipError_t launch_flash_attention(const FlashLaunch &a, hipStream_t s) {
     const int total = a.H * a.nqt;
     const int per_xcd = (total + 7) / 8;
     const size_t dyn = 4 * ((size_t)a.nkt + 4);
-    flash_fwd_kernel<<<8 * per_xcd, kNW * 64, dyn, s>>>(a);
+    if (!a.queue) {
+        flash_fwd_kernel<<<8 * per_xcd, kNW * 64, dyn, s>>>(a);
+        return hipGetLastError();
+    }
+    // persistent: one workgroup per CU (the LDS admits one)
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    flash_queue_reset_kernel<<<1, 64, 0, s>>>(a.queue);
+    flash_fwd_kernel<<<cus, kNW * 64, dyn, s>>>(a);
+    if (a.split_items > 0) flash_merge_kernel<<<8 * a.split_items * (kBM / 8), 256, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -72,8 +72,20 @@ struct FlashLaunch {
     const int32_t *doc;
     const uint8_t *cls;
     const int32_t *count, *list, *order;
+    // work queue (NULL: one item per workgroup, nothing split): counters of
+    // the persistent workgroups, the key-range split of the last split_items
+    // items of every XCD's share and their partial results (part)
+    int32_t *queue;
+    int32_t split_items;   // S: the last S items of every XCD's share run in parts
+    float *part;
 };
 void flash_tiles(int32_t *tile_m, int32_t *tile_n);
+// bytes of work-queue counters at the start of the flash workspace
+constexpr size_t kFlashQueueBytes = 256;
+// items per XCD whose key range is split, and the work-queue bytes (counters
+// and partial results) the split needs
+int32_t flash_split_items(int32_t H, int32_t L);
+size_t flash_split_bytes(int32_t H, int32_t L);
 // most k-tiles a layout may have for the attention kernel (its LDS tile list)
 int32_t flash_max_k_tiles();
 hipError_t launch_flash_attention(const FlashLaunch &a, hipStream_t s);

@@ -72,7 +72,8 @@ def sample_rows(layout: dict, n_other: int, seed: int, tile: int = 128) -> np.nd
 class AttentionRun:
     """Run the attention path through the C ABI on one layout + Q/K/V."""
 
-    def __init__(self, inp: dict, wq=None, wk=None, device="cuda", pos_scale=(1.0, 1.0, 1.0)):
+    def __init__(self, inp: dict, wq=None, wk=None, device="cuda", pos_scale=(1.0, 1.0, 1.0),
+                 split=True):
         import torch
         from packed_masked_attention_amd import binding as B
         self.B = B
@@ -97,6 +98,9 @@ class AttentionRun:
         self.vt = torch.empty(self.H, D, self.Lp, dtype=torch.bfloat16, device=device)
         self.o = torch.full((self.L, self.H * D), float("nan"), dtype=torch.bfloat16, device=device)
         self.lse = torch.full((self.H, self.L), float("nan"), dtype=torch.float32, device=device)
+        # the flash workspace turns on the key-range split of the last items
+        self.ws = torch.empty(B.pma_flash_workspace_size(self.p, self.L), dtype=torch.uint8,
+                              device=device) if split else None
 
     def prep(self):
         HD = self.H * self.D
@@ -105,7 +109,7 @@ class AttentionRun:
 
     def flash(self):
         self.B.pma_flash_attention(self.p, self.dl, self.qh, self.kh, self.vt, self.o,
-                                   self.H * self.D, self.lse)
+                                   self.H * self.D, self.lse, workspace=self.ws)
 
     def run(self):
         import torch

@@ -62,13 +62,25 @@ def test_host_side_argument_errors(lib):
     p = B.attn_params(4, F=12)
     assert lib.pma_attention_workspace_size(ctypes.byref(p), 100, ctypes.byref(n)) == 7
     p = B.attn_params(56)
+    fw = ctypes.c_size_t()
+    assert lib.pma_flash_workspace_size(ctypes.byref(p), 16384, ctypes.byref(fw)) == 0
+    # 256 B of work-queue counters, then 16 split items per XCD (of 56 x 64 / 8
+    # = 448) x 4 parts, each 256 rows x (128 channels + max + row sum) fp32
+    assert fw.value == 256 + 8 * 16 * 4 * 256 * 130 * 4
+    # below 192 k-tiles (12288 keys) nothing is split: the counters alone
+    assert lib.pma_flash_workspace_size(ctypes.byref(B.attn_params(2)), 100, ctypes.byref(n)) == 0
+    assert n.value == 256
+    assert lib.pma_flash_workspace_size(ctypes.byref(B.attn_params(2)), 12288, ctypes.byref(n)) == 0
+    # 2 heads x 48 q-tiles: 12 items per XCD, all 12 split
+    assert n.value == 256 + 8 * 12 * 4 * 256 * 130 * 4
+    assert lib.pma_flash_workspace_size(ctypes.byref(p), 0, ctypes.byref(n)) == 2
     assert lib.pma_attention_workspace_size(ctypes.byref(p), 16384, ctypes.byref(n)) == 0
-    assert n.value == 3 * 56 * 16384 * 128 * 2
+    assert n.value == 3 * 56 * 16384 * 128 * 2 + fw.value
     lp = ctypes.c_int32()
     assert lib.pma_attention_padded_len(16385, ctypes.byref(lp)) == 0 and lp.value == 16640
     lay = B.Layout()
     assert lib.pma_flash_attention(ctypes.byref(p), ctypes.byref(lay), None, None, None, None, 0,
-                                   None, None) == 1
+                                   None, None, 0, None) == 1
     # a layout past the kernel's LDS tile-list capacity is refused on the host
     tm, tn = ctypes.c_int32(), ctypes.c_int32()
     lib.pma_attention_tiles(ctypes.byref(tm), ctypes.byref(tn))
@@ -77,8 +89,17 @@ def test_host_side_argument_errors(lib):
     big = B.Layout(nk * tn.value, 1, tm.value, tn.value, (nk * tn.value + tm.value - 1) // tm.value,
                    nk, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake)
     assert lib.pma_flash_attention(ctypes.byref(p), ctypes.byref(big), fake, fake, fake, fake,
-                                   56 * 128, None, None) == 2
+                                   56 * 128, None, None, 0, None) == 2
     assert "k-tiles" in lib.pma_last_error().decode()
+    # a flash workspace that is misaligned or too small
+    ok = B.Layout(8192, 1, tm.value, tn.value, 8192 // tm.value, 8192 // tn.value, fake, fake, fake,
+                  fake, fake, fake, fake, fake, fake, fake)
+    assert lib.pma_flash_workspace_size(ctypes.byref(p), 8192, ctypes.byref(fw)) == 0
+    assert lib.pma_flash_attention(ctypes.byref(p), ctypes.byref(ok), fake, fake, fake, fake,
+                                   56 * 128, None, ctypes.c_void_p(256 + 64), fw.value, None) == 3
+    assert lib.pma_flash_attention(ctypes.byref(p), ctypes.byref(ok), fake, fake, fake, fake,
+                                   56 * 128, None, fake, fw.value - 1, None) == 4
+    assert "flash workspace" in lib.pma_last_error().decode()
 
 
 def test_io_path_host_side_argument_errors(lib):
