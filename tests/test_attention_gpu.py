@@ -232,3 +232,33 @@ def test_attention_key_range_split(case):
     split.flash()
     torch.cuda.synchronize()
     assert torch.equal(split.o.view(torch.int16), o1.view(torch.int16))
+
+
+def test_attention_work_queue_graph_replays():
+    """The work-queue path (counters cleared by a kernel, parts merged) inside
+    a HIP graph: every replay, with eager work and synchronisations between,
+    equals the eager call bit for bit."""
+    import torch
+    inp = _random_inputs(63, 12500, 2, 0.05, False)
+    say("attention work queue in a HIP graph, L=12500 H=2")
+    r = AttentionRun(inp).run()
+    ref = r.o.clone()
+    other = AttentionRun(_random_inputs(64, 12400, 2, 0.1, True))
+    other.prep()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        r.flash()                       # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        r.flash()
+    for rep in range(3):
+        r.o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(r.o.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+        other.flash()                   # eager work on another workspace between replays
+        torch.cuda.synchronize()
