@@ -225,133 +225,315 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
     __shared__ int2 work;
     (void)arg;   // read through the kernarg segment below
     for (int iter = 0;; ++iter) {
-    // the launch arguments, read again for every item, so that none of them
-    // stays live across the work loop
-    kernarg_launch ap = (kernarg_launch)__builtin_amdgcn_kernarg_segment_ptr();
-    asm volatile("" : "+s"(ap));
-    FlashLaunch a;
-    __builtin_memcpy(&a, ap, sizeof(FlashLaunch));
-    if (tid == 0) work = next_work(a, xcd_hw, iter);
-    __syncthreads();
-    const int item = __builtin_amdgcn_readfirstlane(work.x);
-    const int part = __builtin_amdgcn_readfirstlane(work.y);
-    __syncthreads();   // every wave has read `work` before it is written again
-    if (item < 0) break;
-    const int total = a.H * a.nqt;
-    const int per_xcd = (total + 7) / 8;
-    const int head = item / a.nqt;
-    const int qt = a.order[item % a.nqt];
-    const int full = a.count[qt];
-    const int beg = part < 0 ? 0 : part * full / kSplitParts;
-    const int cnt = part < 0 ? full : (part + 1) * full / kSplitParts - beg;
-    // a part's partial result: slot of (owning XCD, split item, part)
-    const int owner = item / per_xcd, sidx = item % per_xcd - (per_xcd - a.split_items);
-    float *pres = part < 0 ? nullptr
-                           : a.part + (int64_t)((owner * a.split_items + sidx) * kSplitParts + part) *
-                                          kPartFloats;
-    if (cnt == 0) {
-        // an empty key range: a part with no weight
-        if (tid < kBM) {
-            pres[kBM * kD + 2 * tid] = -INFINITY;
-            pres[kBM * kD + 2 * tid + 1] = 0.f;
+        // the launch arguments, read again for every item, so that none of them
+        // stays live across the work loop
+        kernarg_launch ap = (kernarg_launch)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(ap));
+        FlashLaunch a;
+        __builtin_memcpy(&a, ap, sizeof(FlashLaunch));
+        if (tid == 0) work = next_work(a, xcd_hw, iter);
+        __syncthreads();
+        const int item = __builtin_amdgcn_readfirstlane(work.x);
+        const int part = __builtin_amdgcn_readfirstlane(work.y);
+        __syncthreads();   // every wave has read `work` before it is written again
+        if (item < 0) break;
+        const int total = a.H * a.nqt;
+        const int per_xcd = (total + 7) / 8;
+        const int head = item / a.nqt;
+        const int qt = a.order[item % a.nqt];
+        const int full = a.count[qt];
+        const int beg = part < 0 ? 0 : part * full / kSplitParts;
+        const int cnt = part < 0 ? full : (part + 1) * full / kSplitParts - beg;
+        // a part's partial result: slot of (owning XCD, split item, part)
+        const int owner = item / per_xcd, sidx = item % per_xcd - (per_xcd - a.split_items);
+        float *pres = part < 0 ? nullptr
+                               : a.part + (int64_t)((owner * a.split_items + sidx) * kSplitParts + part) *
+                                              kPartFloats;
+        if (cnt == 0) {
+            // an empty key range: a part with no weight
+            if (tid < kBM) {
+                pres[kBM * kD + 2 * tid] = -INFINITY;
+                pres[kBM * kD + 2 * tid + 1] = 0.f;
+            }
+            continue;
         }
-        continue;
-    }
-    {
-        const int32_t *list = a.list + (int64_t)qt * a.nkt + beg;
-        const uint8_t *cls = a.cls + (int64_t)qt * a.nkt;
-        for (int i = tid; i < cnt; i += kNW * 64) {
-            const int kt = list[i];
-            const bool m = cls[kt] != PMA_TILE_FULL || (kt + 1) * kBN > a.L;
-            tlist[i] = kt | (m ? (1 << 30) : 0);
+        {
+            const int32_t *list = a.list + (int64_t)qt * a.nkt + beg;
+            const uint8_t *cls = a.cls + (int64_t)qt * a.nkt;
+            for (int i = tid; i < cnt; i += kNW * 64) {
+                const int kt = list[i];
+                const bool m = cls[kt] != PMA_TILE_FULL || (kt + 1) * kBN > a.L;
+                tlist[i] = kt | (m ? (1 << 30) : 0);
+            }
+            if (tid < 4) tlist[cnt + tid] = 0;
         }
-        if (tid < 4) tlist[cnt + tid] = 0;
-    }
-    __syncthreads();   // the list is read by every wave from here on
+        __syncthreads();   // the list is read by every wave from here on
 
-    const __amdgpu_buffer_rsrc_t krs =
-        make_rsrc(a.kh + (int64_t)head * a.Lp * kD, (uint32_t)a.Lp * kD * 2u);
-    const __amdgpu_buffer_rsrc_t vrs =
-        make_rsrc(a.vt + (int64_t)head * kD * a.Lp, (uint32_t)a.Lp * kD * 2u);
-    // keys past the sequence read as document 0 here; the mask adds the bound
-    const __amdgpu_buffer_rsrc_t drs = make_rsrc(a.doc, (uint32_t)a.L * 4u);
+        const __amdgpu_buffer_rsrc_t krs =
+            make_rsrc(a.kh + (int64_t)head * a.Lp * kD, (uint32_t)a.Lp * kD * 2u);
+        const __amdgpu_buffer_rsrc_t vrs =
+            make_rsrc(a.vt + (int64_t)head * kD * a.Lp, (uint32_t)a.Lp * kD * 2u);
+        // keys past the sequence read as document 0 here; the mask adds the bound
+        const __amdgpu_buffer_rsrc_t drs = make_rsrc(a.doc, (uint32_t)a.L * 4u);
 
-    // ---- Q^T fragments: lane holds query row l32, channels 16c + 8*hi + [0, 8)
-    const int q0 = qt * kBM + wave * 32;
-    bf16x8 qf[8];
-    {
-        const uint16_t *qrow = a.qh + ((int64_t)head * a.Lp + q0 + l32) * kD + 8 * hi;
+        // ---- Q^T fragments: lane holds query row l32, channels 16c + 8*hi + [0, 8)
+        const int q0 = qt * kBM + wave * 32;
+        bf16x8 qf[8];
+        {
+            const uint16_t *qrow = a.qh + ((int64_t)head * a.Lp + q0 + l32) * kD + 8 * hi;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * c);
-    }
-    const int qrow = q0 + l32;
-    const int dq = (uint32_t)qrow < (uint32_t)a.L ? a.doc[qrow] : 0;
-
-    // ---- LDS-DMA lane offsets.  Wave-instruction j of the K tile fills rows
-    // 4j..4j+3 (lane l: row 4j + l/16, position l%16); of the V^T tile, rows
-    // 8j..8j+7 (lane l: row 8j + l/8, position l%8).  Each lane fetches the
-    // chunk the swizzle places at its position; the tile's own offset
-    // (kt * 64 keys) is the SGPR offset.
-    uint32_t kvo[kKI], vvo[kKI];
-#pragma unroll
-    for (int i = 0; i < kKI; ++i) {
-        const int j = wave * kKI + i;
-        const int kr = 4 * j + (lane >> 4), kp = lane & 15;
-        kvo[i] = 2u * (uint32_t)(kr * kD + 8 * k_pos(kr, kp));
-        const int vr = 8 * j + (lane >> 3), vp = lane & 7;
-        vvo[i] = 2u * ((uint32_t)vr * (uint32_t)a.Lp + 8u * v_pos(vr, vp));
-    }
-    const uint32_t dvo = 4u * (uint32_t)(wave * 8 + (lane & 7));
-    // wave-instruction i of this wave's share of a K or V^T tile, and the
-    // document ids of a V tile's keys (8 per wave: lanes 0..7)
-    auto dma_k1 = [&](int kt, uint16_t *dst, int i) __attribute__((always_inline)) {
-        dma16(krs, (lds_void *)&dst[(wave * kKI + i) * 512], kvo[i], (uint32_t)kt * (kBN * kD * 2));
-    };
-    auto dma_v1 = [&](int kt, uint16_t *dst, int i) __attribute__((always_inline)) {
-        dma16(vrs, (lds_void *)&dst[(wave * kKI + i) * 512], vvo[i], (uint32_t)kt * (kBN * 2));
-    };
-    auto dma_id = [&](int kt, uint16_t *dst) __attribute__((always_inline)) {
-        if (lane < 8) dma4(drs, (lds_void *)&dst[kTileElems + wave * 16], dvo, (uint32_t)kt * (kBN * 4));
-    };
-    auto dma_k = [&](int kt, uint16_t *dst) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < kKI; ++i) dma_k1(kt, dst, i);
-    };
-    auto dma_v = [&](int kt, uint16_t *dst) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < kKI; ++i) dma_v1(kt, dst, i);
-        dma_id(kt, dst);
-    };
-
-    const int krow = k_slab_row(l32);
-    const float c2 = a.scale_log2;
-
-    // ---- per-row state: lazy reference max (log2 units), partial row sum, O^T
-    float mref = -INFINITY, lsum = 0.f;
-    f32x16 o[4];
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
-    f32x16 s[2];     // S(t)^T, 2 slabs of 32 keys
-    bf16x8 pf[4];    // P(t)^T in bf16, 4 chunks of 16 keys
-    bf16x8 vpre[kVPre];
-
-    // ---- MFMA phase: O^T += V(t-1)^T P(t-1)^T (when withpv), S(t) = K(t) Q^T
-    auto gphase = [&](bool withpv, const uint16_t *vr, const uint16_t *kr, int dk, uint16_t *dks,
-                      int dv, uint16_t *dvs) __attribute__((always_inline)) {
-        // the document-id DMA (8 lanes) ahead of the scheduled region: its
-        // lane branch would split the MFMA block
-        dma_id(dv, dvs);
-        __builtin_amdgcn_s_setprio(1);
-        if (!withpv) {
-            // the first tile has no PV half to spread them over
-            dma_k(dk, dks);
-#pragma unroll
-            for (int i = 0; i < kKI; ++i) dma_v1(dv, dvs, i);
+            for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * c);
         }
-        if (withpv) {
-            // channel blocks interleaved so consecutive MFMAs are independent
+        const int qrow = q0 + l32;
+        const int dq = (uint32_t)qrow < (uint32_t)a.L ? a.doc[qrow] : 0;
+
+        // ---- LDS-DMA lane offsets.  Wave-instruction j of the K tile fills rows
+        // 4j..4j+3 (lane l: row 4j + l/16, position l%16); of the V^T tile, rows
+        // 8j..8j+7 (lane l: row 8j + l/8, position l%8).  Each lane fetches the
+        // chunk the swizzle places at its position; the tile's own offset
+        // (kt * 64 keys) is the SGPR offset.
+        uint32_t kvo[kKI], vvo[kKI];
+#pragma unroll
+        for (int i = 0; i < kKI; ++i) {
+            const int j = wave * kKI + i;
+            const int kr = 4 * j + (lane >> 4), kp = lane & 15;
+            kvo[i] = 2u * (uint32_t)(kr * kD + 8 * k_pos(kr, kp));
+            const int vr = 8 * j + (lane >> 3), vp = lane & 7;
+            vvo[i] = 2u * ((uint32_t)vr * (uint32_t)a.Lp + 8u * v_pos(vr, vp));
+        }
+        const uint32_t dvo = 4u * (uint32_t)(wave * 8 + (lane & 7));
+        // wave-instruction i of this wave's share of a K or V^T tile, and the
+        // document ids of a V tile's keys (8 per wave: lanes 0..7)
+        auto dma_k1 = [&](int kt, uint16_t *dst, int i) __attribute__((always_inline)) {
+            dma16(krs, (lds_void *)&dst[(wave * kKI + i) * 512], kvo[i], (uint32_t)kt * (kBN * kD * 2));
+        };
+        auto dma_v1 = [&](int kt, uint16_t *dst, int i) __attribute__((always_inline)) {
+            dma16(vrs, (lds_void *)&dst[(wave * kKI + i) * 512], vvo[i], (uint32_t)kt * (kBN * 2));
+        };
+        auto dma_id = [&](int kt, uint16_t *dst) __attribute__((always_inline)) {
+            if (lane < 8) dma4(drs, (lds_void *)&dst[kTileElems + wave * 16], dvo, (uint32_t)kt * (kBN * 4));
+        };
+        auto dma_k = [&](int kt, uint16_t *dst) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < kKI; ++i) dma_k1(kt, dst, i);
+        };
+        auto dma_v = [&](int kt, uint16_t *dst) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < kKI; ++i) dma_v1(kt, dst, i);
+            dma_id(kt, dst);
+        };
+
+        const int krow = k_slab_row(l32);
+        const float c2 = a.scale_log2;
+
+        // ---- per-row state: lazy reference max (log2 units), partial row sum, O^T
+        float mref = -INFINITY, lsum = 0.f;
+        f32x16 o[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
+        f32x16 s[2];     // S(t)^T, 2 slabs of 32 keys
+        bf16x8 pf[4];    // P(t)^T in bf16, 4 chunks of 16 keys
+        bf16x8 vpre[kVPre];
+
+        // ---- MFMA phase: O^T += V(t-1)^T P(t-1)^T (when withpv), S(t) = K(t) Q^T
+        auto gphase = [&](bool withpv, const uint16_t *vr, const uint16_t *kr, int dk, uint16_t *dks,
+                          int dv, uint16_t *dvs) __attribute__((always_inline)) {
+            // the document-id DMA (8 lanes) ahead of the scheduled region: its
+            // lane branch would split the MFMA block
+            dma_id(dv, dvs);
+            __builtin_amdgcn_s_setprio(1);
+            if (!withpv) {
+                // the first tile has no PV half to spread them over
+                dma_k(dk, dks);
+#pragma unroll
+                for (int i = 0; i < kKI; ++i) dma_v1(dv, dvs, i);
+            }
+            if (withpv) {
+                // channel blocks interleaved so consecutive MFMAs are independent
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+                    for (int db = 0; db < 4; ++db) {
+                        const int d = 32 * db + l32;
+                        const int f = cc * 4 + db;
+                        const bf16x8 vf = f < kVPre ? vpre[f < kVPre ? f : 0]
+                                                    : *reinterpret_cast<const bf16x8 *>(vr + d * kBN + 8 * v_pos(d, 2 * cc + hi));
+                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[cc], o[db], 0, 0, 0);
+                        // this wave's share of the ring refill, spread over the
+                        // phase rather than issued in one burst (kKI == 2)
+                        if (f == 2) dma_k1(dk, dks, 0);
+                        if (f == 8) dma_k1(dk, dks, 1);
+                        if (f == 14) dma_v1(dv, dvs, 0);
+                    }
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const int r = 32 * kb + krow;
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kr + r * kD + 8 * k_pos(r, 2 * c + hi));
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
+                    if (withpv && c == 2 && kb == 1) dma_v1(dv, dvs, 1);
+                }
+            // LDS fragment reads run kReadAhead ahead of their MFMAs; the DMA
+            // instructions sit between MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (i == 2 || i == 8 || i == 14 || i == 21)
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+            __builtin_amdgcn_s_setprio(0);
+        };
+
+        // ---- softmax phase of tile t (list entry e, V(t) slot vn): mask,
+        // lazy-max softmax -> P(t)^T in bf16, O rescale
+        auto sphase = [&](int e, const uint16_t *vn) __attribute__((always_inline)) {
+            // V(t) fragments for the first MFMAs of the next PV, read while the
+            // softmax runs
+#pragma unroll
+            for (int f = 0; f < kVPre; ++f) {
+                const int cc = f / 4, db = f % 4;
+                const int d = 32 * db + l32;
+                vpre[f] = *reinterpret_cast<const bf16x8 *>(vn + d * kBN + 8 * v_pos(d, 2 * cc + hi));
+            }
+            if (e >> 30) {
+                // document / bounds mask of a PARTIAL or ragged tile.  The lane's
+                // 32 keys are the bytes 16g + 8*hi (g = 0..3) of the tile's
+                // ballot; gather them so bit 16*kb + v is register (kb, v)
+                const int key = (e & kMask) * kBN + lane;
+                const int dk = (uint32_t)key < (uint32_t)a.L
+                                   ? reinterpret_cast<const int32_t *>(vn + kTileElems)[lane] : -1;
+                // both ballots over the whole wave (lane = key), then the row's pick:
+                // a ballot under a divergent select would drop the other lanes' keys
+                const uint64_t padm = __ballot(dk == 1), realm = __ballot(dk == 0);
+                const uint64_t allow = dq ? padm : realm;
+                const uint32_t lo = (uint32_t)allow, hw = (uint32_t)(allow >> 32);
+                const uint32_t sh = 8u * hi;
+                const uint32_t m32 = ((lo >> sh) & 0xffu) | (((lo >> (16 + sh)) & 0xffu) << 8) |
+                                     (((hw >> sh) & 0xffu) << 16) | (((hw >> (16 + sh)) & 0xffu) << 24);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        if (!((m32 >> (16 * kb + v)) & 1u)) s[kb][v] = -INFINITY;
+            }
+            // row max over four independent chains of IEEE maximum, which the
+            // compiler fuses into three-input v_maximum3 on the raw MFMA results
+            // (fmaxf would canonicalise every input first)
+            float m4[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int b = 8 * (g & 1);
+                float m = __builtin_elementwise_maximum(s[g >> 1][b], s[g >> 1][b + 1]);
+#pragma unroll
+                for (int k = 2; k < 8; k += 2)
+                    m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, s[g >> 1][b + k]),
+                                                      s[g >> 1][b + k + 1]);
+                m4[g] = m;
+            }
+            float mx = __builtin_elementwise_maximum(
+                __builtin_elementwise_maximum(__builtin_elementwise_maximum(m4[0], m4[1]), m4[2]), m4[3]);
+            mx = half_max(mx) * c2;
+            const bool need = mx > mref + 8.0f;
+            const float mnew = need ? mx : mref;
+            const float alpha = need ? __builtin_amdgcn_exp2f(mref - mnew) : 1.0f;
+            mref = mnew;
+            const float mu = (mnew == -INFINITY) ? 0.f : mnew;
+            // probabilities; the row sum (four independent chains, each started
+            // by its first pair rather than by adding to zero) is taken over the
+            // fp32 values before their rounding to bf16
+            float rsp[4];
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                bf16x2 pp[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[cc >> 1][8 * (cc & 1) + 2 * t], c2, -mu));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[cc >> 1][8 * (cc & 1) + 2 * t + 1], c2, -mu));
+                    const f32x2 pv = {p0, p1};
+                    pp[t] = __builtin_convertvector(pv, bf16x2);
+                    rsp[t] = cc ? rsp[t] + (p0 + p1) : p0 + p1;
+                }
+                pf[cc] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+                                                 __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
+                                                 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            lsum = fmaf(lsum, alpha, (rsp[0] + rsp[1]) + (rsp[2] + rsp[3]));
+            // keep the softmax in this phase: without a use here the compiler
+            // sinks it past the barrier into the MFMA phase that consumes P
+            asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3]), "v"(lsum));
+            if (__ballot(need)) {
+#pragma unroll
+                for (int db = 0; db < 4; ++db) o[db] *= alpha;
+            }
+        };
+
+        // ---- prologue: K(0..2), V(0..1) resident
+        dma_k(__builtin_amdgcn_readfirstlane(tlist[0]) & kMask, ks0);
+        dma_k(__builtin_amdgcn_readfirstlane(tlist[1]) & kMask, ks1);
+        dma_k(__builtin_amdgcn_readfirstlane(tlist[2]) & kMask, ks2);
+        dma_v(__builtin_amdgcn_readfirstlane(tlist[0]) & kMask, vs0);
+        dma_v(__builtin_amdgcn_readfirstlane(tlist[1]) & kMask, vs1);
+        PMA_PHASE_END(0);
+
+        // Global phase p: group 0 runs G(t) at p = 2t and S(t) at 2t + 1; group 1
+        // runs one phase later.  Tile x sits in ring slot x % 4.  K(t) is read in
+        // phases 2t, 2t+1; V(t) in 2t+1 .. 2t+3.  Each wave issues its share of
+        // DMA(t) = {K(t+3), V(t+2)} during its G(t) (the slots of K(t-1) and
+        // V(t-2), both done with by the end of phase 2t-1); the waits at
+        // phase ends (two batches may stay in flight after G, one after S) make
+        // DMA(t) land by the end of phase 2t+4, before either tile is first read.
+        if (grp == 1) PMA_PHASE_END(0);
+
+        // list entries of the current tile t: ce = entry t, ck = entry t+3 (the
+        // K tile to fetch), cv = entry t+2 (the V tile to fetch).  The next
+        // tile's are read during the softmax phase, so the MFMA phase starts
+        // without an LDS wait.
+        int ce = __builtin_amdgcn_readfirstlane(tlist[0]);
+        int ck = __builtin_amdgcn_readfirstlane(tlist[3]);
+        int cv = __builtin_amdgcn_readfirstlane(tlist[2]);
+        // k_r = K(t), k_m = slot of K(t-1) <- K(t+3); v_r = V(t), v_p = V(t-1),
+        // v_q = slot of V(t-2) <- V(t+2)
+        auto tile = [&](int t, bool withpv, uint16_t *k_r, uint16_t *k_m, uint16_t *v_r,
+                        uint16_t *v_p, uint16_t *v_q) __attribute__((always_inline)) {
+            const int e = ce;
+            gphase(withpv, v_p, k_r, ck & kMask, k_m, cv & kMask, v_q);
+            PMA_PHASE_END(2 * kNDMA);
+            const int ne = tlist[t + 1], nk = tlist[t + 4], nv = tlist[t + 3];
+            sphase(e, v_r);
+            ce = __builtin_amdgcn_readfirstlane(ne);
+            ck = __builtin_amdgcn_readfirstlane(nk);
+            cv = __builtin_amdgcn_readfirstlane(nv);
+            PMA_PHASE_END(kNDMA);
+        };
+        //    t, pv,   K(t) K(t-1) V(t) V(t-1) V(t-2)
+        tile(0, false, ks0, ks3, vs0, vs3, vs2);
+        int t = 1;
+        for (; t + 4 <= cnt; t += 4) {
+            tile(t, true, ks1, ks0, vs1, vs0, vs3);
+            tile(t + 1, true, ks2, ks1, vs2, vs1, vs0);
+            tile(t + 2, true, ks3, ks2, vs3, vs2, vs1);
+            tile(t + 3, true, ks0, ks3, vs0, vs3, vs2);
+        }
+        // t % 4 == 1 here
+        if (t < cnt) tile(t, true, ks1, ks0, vs1, vs0, vs3), ++t;
+        if (t < cnt) tile(t, true, ks2, ks1, vs2, vs1, vs0), ++t;
+        if (t < cnt) tile(t, true, ks3, ks2, vs3, vs2, vs1), ++t;
+
+        // ---- final PV of the last tile (its V sits in slot (cnt - 1) % 4)
+        {
+            const int r = (cnt - 1) & 3;
+            const uint16_t *vr = r == 0 ? vs0 : (r == 1 ? vs1 : (r == 2 ? vs2 : vs3));
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
@@ -361,231 +543,49 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
                     const bf16x8 vf = f < kVPre ? vpre[f < kVPre ? f : 0]
                                                 : *reinterpret_cast<const bf16x8 *>(vr + d * kBN + 8 * v_pos(d, 2 * cc + hi));
                     o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[cc], o[db], 0, 0, 0);
-                    // this wave's share of the ring refill, spread over the
-                    // phase rather than issued in one burst (kKI == 2)
-                    if (f == 2) dma_k1(dk, dks, 0);
-                    if (f == 8) dma_k1(dk, dks, 1);
-                    if (f == 14) dma_v1(dv, dvs, 0);
                 }
+            __builtin_amdgcn_s_setprio(0);
         }
+        // no LDS-DMA may still be writing when the workgroup's LDS is released;
+        // group 0 matches group 1's extra barrier
+        PMA_WAIT_VM(0);
+        if (grp == 0) PMA_PHASE_END(0);
+
+        // ---- epilogue: O row = O^T column / row sum; register v of d-block db is
+        // channel 32*db + 8*(v/4) + 4*hi + v%4
+        const float lt = half_sum(lsum);
+        if (part >= 0) {
+            // a part: unnormalised O (reference mref) and the row sum, for the merge
+            const int r = wave * 32 + l32;
+            float *orow = pres + r * kD + 4 * hi;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const int r = 32 * kb + krow;
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kr + r * kD + 8 * k_pos(r, 2 * c + hi));
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
-                if (withpv && c == 2 && kb == 1) dma_v1(dv, dvs, 1);
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 w = {o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+                    *reinterpret_cast<f32x4 *>(orow + 32 * db + 8 * g) = w;
+                }
+            if (hi == 0) {
+                pres[kBM * kD + 2 * r] = mref;
+                pres[kBM * kD + 2 * r + 1] = lt;
             }
-        // LDS fragment reads run kReadAhead ahead of their MFMAs; the DMA
-        // instructions sit between MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if (i == 2 || i == 8 || i == 14 || i == 21)
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            continue;
         }
-        __builtin_amdgcn_s_setprio(0);
-    };
-
-    // ---- softmax phase of tile t (list entry e, V(t) slot vn): mask,
-    // lazy-max softmax -> P(t)^T in bf16, O rescale
-    auto sphase = [&](int e, const uint16_t *vn) __attribute__((always_inline)) {
-        // V(t) fragments for the first MFMAs of the next PV, read while the
-        // softmax runs
+        const float inv = 1.0f / lt;
+        if (qrow < a.L) {
+            uint16_t *orow = a.o + (int64_t)qrow * a.o_ld + head * kD + 4 * hi;
 #pragma unroll
-        for (int f = 0; f < kVPre; ++f) {
-            const int cc = f / 4, db = f % 4;
-            const int d = 32 * db + l32;
-            vpre[f] = *reinterpret_cast<const bf16x8 *>(vn + d * kBN + 8 * v_pos(d, 2 * cc + hi));
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    uint2 w;
+                    w.x = pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+                    w.y = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+                    *reinterpret_cast<uint2 *>(orow + 32 * db + 8 * g) = w;
+                }
+            if (a.lse && hi == 0)
+                a.lse[(int64_t)head * a.L + qrow] = (mref + __log2f(lt)) * 0.69314718055994531f;
         }
-        if (e >> 30) {
-            // document / bounds mask of a PARTIAL or ragged tile.  The lane's
-            // 32 keys are the bytes 16g + 8*hi (g = 0..3) of the tile's
-            // ballot; gather them so bit 16*kb + v is register (kb, v)
-            const int key = (e & kMask) * kBN + lane;
-            const int dk = (uint32_t)key < (uint32_t)a.L
-                               ? reinterpret_cast<const int32_t *>(vn + kTileElems)[lane] : -1;
-            // both ballots over the whole wave (lane = key), then the row's pick:
-            // a ballot under a divergent select would drop the other lanes' keys
-            const uint64_t padm = __ballot(dk == 1), realm = __ballot(dk == 0);
-            const uint64_t allow = dq ? padm : realm;
-            const uint32_t lo = (uint32_t)allow, hw = (uint32_t)(allow >> 32);
-            const uint32_t sh = 8u * hi;
-            const uint32_t m32 = ((lo >> sh) & 0xffu) | (((lo >> (16 + sh)) & 0xffu) << 8) |
-                                 (((hw >> sh) & 0xffu) << 16) | (((hw >> (16 + sh)) & 0xffu) << 24);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    if (!((m32 >> (16 * kb + v)) & 1u)) s[kb][v] = -INFINITY;
-        }
-        // row max over four independent chains of IEEE maximum, which the
-        // compiler fuses into three-input v_maximum3 on the raw MFMA results
-        // (fmaxf would canonicalise every input first)
-        float m4[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int b = 8 * (g & 1);
-            float m = __builtin_elementwise_maximum(s[g >> 1][b], s[g >> 1][b + 1]);
-#pragma unroll
-            for (int k = 2; k < 8; k += 2)
-                m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, s[g >> 1][b + k]),
-                                                  s[g >> 1][b + k + 1]);
-            m4[g] = m;
-        }
-        float mx = __builtin_elementwise_maximum(
-            __builtin_elementwise_maximum(__builtin_elementwise_maximum(m4[0], m4[1]), m4[2]), m4[3]);
-        mx = half_max(mx) * c2;
-        const bool need = mx > mref + 8.0f;
-        const float mnew = need ? mx : mref;
-        const float alpha = need ? __builtin_amdgcn_exp2f(mref - mnew) : 1.0f;
-        mref = mnew;
-        const float mu = (mnew == -INFINITY) ? 0.f : mnew;
-        // probabilities; the row sum (four independent chains, each started
-        // by its first pair rather than by adding to zero) is taken over the
-        // fp32 values before their rounding to bf16
-        float rsp[4];
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-            bf16x2 pp[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[cc >> 1][8 * (cc & 1) + 2 * t], c2, -mu));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[cc >> 1][8 * (cc & 1) + 2 * t + 1], c2, -mu));
-                const f32x2 pv = {p0, p1};
-                pp[t] = __builtin_convertvector(pv, bf16x2);
-                rsp[t] = cc ? rsp[t] + (p0 + p1) : p0 + p1;
-            }
-            pf[cc] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
-                                             __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
-                                             0, 1, 2, 3, 4, 5, 6, 7);
-        }
-        lsum = fmaf(lsum, alpha, (rsp[0] + rsp[1]) + (rsp[2] + rsp[3]));
-        // keep the softmax in this phase: without a use here the compiler
-        // sinks it past the barrier into the MFMA phase that consumes P
-        asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3]), "v"(lsum));
-        if (__ballot(need)) {
-#pragma unroll
-            for (int db = 0; db < 4; ++db) o[db] *= alpha;
-        }
-    };
-
-    // ---- prologue: K(0..2), V(0..1) resident
-    dma_k(__builtin_amdgcn_readfirstlane(tlist[0]) & kMask, ks0);
-    dma_k(__builtin_amdgcn_readfirstlane(tlist[1]) & kMask, ks1);
-    dma_k(__builtin_amdgcn_readfirstlane(tlist[2]) & kMask, ks2);
-    dma_v(__builtin_amdgcn_readfirstlane(tlist[0]) & kMask, vs0);
-    dma_v(__builtin_amdgcn_readfirstlane(tlist[1]) & kMask, vs1);
-    PMA_PHASE_END(0);
-
-    // Global phase p: group 0 runs G(t) at p = 2t and S(t) at 2t + 1; group 1
-    // runs one phase later.  Tile x sits in ring slot x % 4.  K(t) is read in
-    // phases 2t, 2t+1; V(t) in 2t+1 .. 2t+3.  Each wave issues its share of
-    // DMA(t) = {K(t+3), V(t+2)} during its G(t) (the slots of K(t-1) and
-    // V(t-2), both done with by the end of phase 2t-1); the waits at
-    // phase ends (two batches may stay in flight after G, one after S) make
-    // DMA(t) land by the end of phase 2t+4, before either tile is first read.
-    if (grp == 1) PMA_PHASE_END(0);
-
-    // list entries of the current tile t: ce = entry t, ck = entry t+3 (the
-    // K tile to fetch), cv = entry t+2 (the V tile to fetch).  The next
-    // tile's are read during the softmax phase, so the MFMA phase starts
-    // without an LDS wait.
-    int ce = __builtin_amdgcn_readfirstlane(tlist[0]);
-    int ck = __builtin_amdgcn_readfirstlane(tlist[3]);
-    int cv = __builtin_amdgcn_readfirstlane(tlist[2]);
-    // k_r = K(t), k_m = slot of K(t-1) <- K(t+3); v_r = V(t), v_p = V(t-1),
-    // v_q = slot of V(t-2) <- V(t+2)
-    auto tile = [&](int t, bool withpv, uint16_t *k_r, uint16_t *k_m, uint16_t *v_r,
-                    uint16_t *v_p, uint16_t *v_q) __attribute__((always_inline)) {
-        const int e = ce;
-        gphase(withpv, v_p, k_r, ck & kMask, k_m, cv & kMask, v_q);
-        PMA_PHASE_END(2 * kNDMA);
-        const int ne = tlist[t + 1], nk = tlist[t + 4], nv = tlist[t + 3];
-        sphase(e, v_r);
-        ce = __builtin_amdgcn_readfirstlane(ne);
-        ck = __builtin_amdgcn_readfirstlane(nk);
-        cv = __builtin_amdgcn_readfirstlane(nv);
-        PMA_PHASE_END(kNDMA);
-    };
-    //    t, pv,   K(t) K(t-1) V(t) V(t-1) V(t-2)
-    tile(0, false, ks0, ks3, vs0, vs3, vs2);
-    int t = 1;
-    for (; t + 4 <= cnt; t += 4) {
-        tile(t, true, ks1, ks0, vs1, vs0, vs3);
-        tile(t + 1, true, ks2, ks1, vs2, vs1, vs0);
-        tile(t + 2, true, ks3, ks2, vs3, vs2, vs1);
-        tile(t + 3, true, ks0, ks3, vs0, vs3, vs2);
-    }
-    // t % 4 == 1 here
-    if (t < cnt) tile(t, true, ks1, ks0, vs1, vs0, vs3), ++t;
-    if (t < cnt) tile(t, true, ks2, ks1, vs2, vs1, vs0), ++t;
-    if (t < cnt) tile(t, true, ks3, ks2, vs3, vs2, vs1), ++t;
-
-    // ---- final PV of the last tile (its V sits in slot (cnt - 1) % 4)
-    {
-        const int r = (cnt - 1) & 3;
-        const uint16_t *vr = r == 0 ? vs0 : (r == 1 ? vs1 : (r == 2 ? vs2 : vs3));
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                const int d = 32 * db + l32;
-                const int f = cc * 4 + db;
-                const bf16x8 vf = f < kVPre ? vpre[f < kVPre ? f : 0]
-                                            : *reinterpret_cast<const bf16x8 *>(vr + d * kBN + 8 * v_pos(d, 2 * cc + hi));
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[cc], o[db], 0, 0, 0);
-            }
-        __builtin_amdgcn_s_setprio(0);
-    }
-    // no LDS-DMA may still be writing when the workgroup's LDS is released;
-    // group 0 matches group 1's extra barrier
-    PMA_WAIT_VM(0);
-    if (grp == 0) PMA_PHASE_END(0);
-
-    // ---- epilogue: O row = O^T column / row sum; register v of d-block db is
-    // channel 32*db + 8*(v/4) + 4*hi + v%4
-    const float lt = half_sum(lsum);
-    if (part >= 0) {
-        // a part: unnormalised O (reference mref) and the row sum, for the merge
-        const int r = wave * 32 + l32;
-        float *orow = pres + r * kD + 4 * hi;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 w = {o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
-                *reinterpret_cast<f32x4 *>(orow + 32 * db + 8 * g) = w;
-            }
-        if (hi == 0) {
-            pres[kBM * kD + 2 * r] = mref;
-            pres[kBM * kD + 2 * r + 1] = lt;
-        }
-        continue;
-    }
-    const float inv = 1.0f / lt;
-    if (qrow < a.L) {
-        uint16_t *orow = a.o + (int64_t)qrow * a.o_ld + head * kD + 4 * hi;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                uint2 w;
-                w.x = pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
-                w.y = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-                *reinterpret_cast<uint2 *>(orow + 32 * db + 8 * g) = w;
-            }
-        if (a.lse && hi == 0)
-            a.lse[(int64_t)head * a.L + qrow] = (mref + __log2f(lt)) * 0.69314718055994531f;
-    }
     }   // work loop
 }
 
