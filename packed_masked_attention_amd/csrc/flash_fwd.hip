@@ -358,8 +358,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
                     for (int db = 0; db < 4; ++db) {
                         const int d = 32 * db + l32;
                         const int f = cc * 4 + db;
-                        const bf16x8 vf = f < kVPre ? vpre[f < kVPre ? f : 0]
-                                                    : *reinterpret_cast<const bf16x8 *>(vr + d * kBN + 8 * v_pos(d, 2 * cc + hi));
+                        const bf16x8 vf =
+                            f < kVPre ? vpre[f < kVPre ? f : 0]
+                                      : *reinterpret_cast<const bf16x8 *>(
+                                            vr + d * kBN + 8 * v_pos(d, 2 * cc + hi));
                         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[cc], o[db], 0, 0, 0);
                         // this wave's share of the ring refill, spread over the
                         // phase rather than issued in one burst (kKI == 2)
@@ -377,7 +379,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     const int r = 32 * kb + krow;
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kr + r * kD + 8 * k_pos(r, 2 * c + hi));
+                    const bf16x8 kf =
+                        *reinterpret_cast<const bf16x8 *>(kr + r * kD + 8 * k_pos(r, 2 * c + hi));
                     s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
                     if (withpv && c == 2 && kb == 1) dma_v1(dv, dvs, 1);
                 }
@@ -458,7 +461,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const float p0 = __builtin_amdgcn_exp2f(fmaf(s[cc >> 1][8 * (cc & 1) + 2 * t], c2, -mu));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[cc >> 1][8 * (cc & 1) + 2 * t + 1], c2, -mu));
+                    const float p1 =
+                        __builtin_amdgcn_exp2f(fmaf(s[cc >> 1][8 * (cc & 1) + 2 * t + 1], c2, -mu));
                     const f32x2 pv = {p0, p1};
                     pp[t] = __builtin_convertvector(pv, bf16x2);
                     rsp[t] = cc ? rsp[t] + (p0 + p1) : p0 + p1;
@@ -540,8 +544,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
                 for (int db = 0; db < 4; ++db) {
                     const int d = 32 * db + l32;
                     const int f = cc * 4 + db;
-                    const bf16x8 vf = f < kVPre ? vpre[f < kVPre ? f : 0]
-                                                : *reinterpret_cast<const bf16x8 *>(vr + d * kBN + 8 * v_pos(d, 2 * cc + hi));
+                    const bf16x8 vf =
+                        f < kVPre ? vpre[f < kVPre ? f : 0]
+                                  : *reinterpret_cast<const bf16x8 *>(vr + d * kBN +
+                                                                      8 * v_pos(d, 2 * cc + hi));
                     o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[cc], o[db], 0, 0, 0);
                 }
             __builtin_amdgcn_s_setprio(0);
