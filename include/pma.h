@@ -216,7 +216,7 @@ pma_status pma_flash_workspace_size(const pma_attn_params *p, int32_t seq_len, s
  *        its probabilities to bf16 against its own running maximum).
  *        Calls that share one workspace must not overlap.
  * The kernel keeps each q-tile's k-tile list in LDS: layouts of more than
- * 7932 k-tiles (seq_len > 507648) return PMA_ERR_SHAPE. */
+ * 6908 k-tiles (seq_len > 442112) return PMA_ERR_SHAPE. */
 pma_status pma_flash_attention(const pma_attn_params *p, const pma_layout *layout,
                                const pma_bf16 *qh, const pma_bf16 *kh, const pma_bf16 *vt,
                                pma_bf16 *o, int64_t o_ld, float *lse, void *workspace,

@@ -89,7 +89,9 @@ constexpr int kSplitParts = 4;             // workgroups per split item
 constexpr int kPartFloats = kBM * kD + 2 * kBM;
 static_assert(kFlashQueueBytes >= 16 * sizeof(int32_t), "the queue reset clears 16 counters");
 // LDS: 4 K slots + 4 V^T slots (each + 64 document ids) + the tile list
-constexpr int kStaticLds = 4 * kTileElems * 2 + 4 * (kTileElems + 2 * kBN) * 2;
+// (the V^T slots are 1024-byte aligned, so each takes 17 KB; 1 KB more covers
+// the work-item word and any placement slack of the static variables)
+constexpr int kStaticLds = 4 * kTileElems * 2 + 4 * (((kTileElems + 2 * kBN) * 2 + 1023) / 1024 * 1024) + 1024;
 constexpr int kLdsBytes = 160 * 1024;      // per workgroup on gfx950
 static_assert(kKI * kNW == 16, "16 KB tiles split over the waves");
 static_assert(kKI == 2, "the MFMA phase spreads two K and two V^T DMA instructions per wave");

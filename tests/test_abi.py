@@ -85,7 +85,7 @@ def test_host_side_argument_errors(lib):
     tm, tn = ctypes.c_int32(), ctypes.c_int32()
     lib.pma_attention_tiles(ctypes.byref(tm), ctypes.byref(tn))
     fake = ctypes.c_void_p(256)
-    nk = 7933
+    nk = 6909   # one more than the LDS tile list holds
     big = B.Layout(nk * tn.value, 1, tm.value, tn.value, (nk * tn.value + tm.value - 1) // tm.value,
                    nk, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake)
     assert lib.pma_flash_attention(ctypes.byref(p), ctypes.byref(big), fake, fake, fake, fake,
