@@ -16,9 +16,10 @@
 // 256x256 preview halves the spatial coordinates).
 //
 // HBM-bound: per (row, head) it reads 3 x 256 B and writes 3 x 256 B.
-// Block = 64 rows x 4 heads.  Each 16-lane group owns one (row, head) of Q or
-// K, 8 channels (16 bytes) per lane, and keeps four such items' loads in
-// flight before it computes them; the sum of squares is reduced across the
+// Block = 64 rows x 4 heads.  The block's V loads (16 per thread) are issued
+// first and stay in flight through the rest.  Each 16-lane group owns one
+// (row, head) of Q or K, 8 channels (16 bytes) per lane, and keeps eight
+// such items' loads in flight before it computes them; the sum of squares is reduced across the
 // group and the RoPE partner channels c +/- F sit F/8 lanes away.  cos/sin of
 // the 64 rows x 3F angles are computed once per block in fp64 (angles reach
 // ~1e3 rad, so no fast-math approximation) and kept in LDS as fp32.  V goes
@@ -45,6 +46,22 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(PrepLaunch a) {
     const int nh = min(kHeads, a.H - h0);
     const int F = a.F;
     const int nang = 3 * F;
+
+    // ---- V loads of every head first: they stay in flight through the
+    // table and the Q/K work
+    u16x8 vraw[kHeads][kRows * 16 / kThreads];
+#pragma unroll
+    for (int hl = 0; hl < kHeads; ++hl)
+#pragma unroll
+        for (int k = 0; k < kRows * 16 / kThreads; ++k) {
+            const int e = tid + k * kThreads;
+            const int rl = e / 16, c8 = e % 16;
+            const int row = r0 + rl;
+            vraw[hl][k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            if (hl < nh && row < a.L)
+                vraw[hl][k] = *reinterpret_cast<const u16x8 *>(a.v + (int64_t)row * a.v_ld +
+                                                               (h0 + hl) * kHeadDim + c8 * 8);
+        }
 
     // ---- cos/sin table of this block's rows
     for (int e = tid; e < kRows * nang; e += kThreads) {
@@ -74,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(PrepLaunch a) {
     const int in_sec = chunk % sec_chunks;
     const bool first_half = in_sec < half_chunks;
     const int f0 = (first_half ? in_sec : in_sec - half_chunks) * 8;
-    constexpr int kB = 4;   // items in flight per 16-lane group
+    constexpr int kB = 8;   // items in flight per 16-lane group
     for (int base = sub; base < n_items; base += kB * (kThreads / 16)) {
         u16x8 raw[kB];
 #pragma unroll
@@ -142,16 +159,15 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(PrepLaunch a) {
     }
 
     // ---- V: stage [64 rows][128] per head, write [128 channels][64 rows]
-    for (int hl = 0; hl < nh; ++hl) {
+#pragma unroll
+    for (int hl = 0; hl < kHeads; ++hl) {
+        if (hl >= nh) break;
         const int h = h0 + hl;
-        for (int e = tid; e < kRows * 16; e += kThreads) {
+#pragma unroll
+        for (int k = 0; k < kRows * 16 / kThreads; ++k) {
+            const int e = tid + k * kThreads;
             const int rl = e / 16, c8 = e % 16;
-            const int row = r0 + rl;
-            u16x8 raw = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (row < a.L)
-                raw = *reinterpret_cast<const u16x8 *>(a.v + (int64_t)row * a.v_ld +
-                                                       h * kHeadDim + c8 * 8);
-            const uint4 w4 = __builtin_bit_cast(uint4, raw);
+            const uint4 w4 = __builtin_bit_cast(uint4, vraw[hl][k]);
             uint32_t *d32 = vtile32 + (rl * kVRow + c8 * 8) / 2;
             d32[0] = w4.x; d32[1] = w4.y; d32[2] = w4.z; d32[3] = w4.w;
         }
