@@ -19,8 +19,9 @@
 // Block = 64 rows x 4 heads.  The block's V loads (16 per thread) are issued
 // first and stay in flight through the rest.  Each 16-lane group owns one
 // (row, head) of Q or K, 8 channels (16 bytes) per lane, and keeps eight
-// such items' loads in flight before it computes them; the sum of squares is reduced across the
-// group and the RoPE partner channels c +/- F sit F/8 lanes away.  cos/sin of
+// such items' loads in flight before it computes them; the sum of squares is
+// reduced across the group and the RoPE partner channels c +/- F sit F/8
+// lanes away, both exchanged by DPP moves inside the 16-lane row.  cos/sin of
 // the 64 rows x 3F angles are computed once per block in fp64 (angles reach
 // ~1e3 rad, so no fast-math approximation) and kept in LDS as fp32.  V goes
 // through LDS and leaves transposed, keys contiguous per (head, channel).
@@ -35,6 +36,22 @@ constexpr int kThreads = 256;
 constexpr int kVRow = kHeadDim + 2;  // LDS row of the V tile in bf16: 65 words, so the
                                      // transposed 2-byte reads spread over the banks
 
+// Cross-lane moves inside a 16-lane row on the VALU (DPP), without the LDS
+// crossbar: lane i reads lane i^1, i^2 (quad permutes) or (i+4)%16, (i+8)%16
+// (row rotations).
+__device__ __forceinline__ float dpp_f(float x, int ctrl_sel) {
+    const int v = __float_as_int(x);
+    int r;
+    switch (ctrl_sel) {
+        case 1: r = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
+        case 2: r = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
+        case 4: r = __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, false); break;  // row_ror:4
+        default: r = __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false); break; // row_ror:8
+    }
+    return __int_as_float(r);
+}
+
+template <int F>
 __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(PrepLaunch a) {
     __shared__ float2 cs[kRows][48];                    // (cos, sin) per row, axis*F + f
     __shared__ uint32_t vtile32[kRows * kVRow / 2];
@@ -44,7 +61,6 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(PrepLaunch a) {
     const int r0 = blockIdx.x * kRows;
     const int h0 = blockIdx.y * kHeads;
     const int nh = min(kHeads, a.H - h0);
-    const int F = a.F;
     const int nang = 3 * F;
 
     // ---- V loads of every head first: they stay in flight through the
@@ -125,10 +141,12 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(PrepLaunch a) {
             float ss = 0.f;
 #pragma unroll
             for (int t = 0; t < 8; ++t) ss = fmaf(x[t], x[t], ss);
-            ss += __shfl_xor(ss, 1, 16);
-            ss += __shfl_xor(ss, 2, 16);
-            ss += __shfl_xor(ss, 4, 16);
-            ss += __shfl_xor(ss, 8, 16);
+            // all 16 lanes end with the group's sum: pairs, quads, then the
+            // quad sums rotated in by 4 and 8
+            ss += dpp_f(ss, 1);
+            ss += dpp_f(ss, 2);
+            ss += dpp_f(ss, 4);
+            ss += dpp_f(ss, 8);
             const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
             const f32x4 w0 = *reinterpret_cast<const f32x4 *>(w + chunk * 8);
             const f32x4 w1 = *reinterpret_cast<const f32x4 *>(w + chunk * 8 + 4);
@@ -141,7 +159,8 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(PrepLaunch a) {
             // partner channels: chunk +/- F/8 within the 16-lane group
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const float pn = __shfl_xor(n[t], half_chunks, 16);
+                // partner channel: F/8 chunks away, i.e. lane ^ 1 (F = 8) or ^ 2 (F = 16)
+                const float pn = dpp_f(n[t], half_chunks);
                 if (rotated) {
                     const float2 e = cs[rl][ax * F + f0 + t];
                     y[t] = first_half ? (n[t] * e.x - pn * e.y) : (n[t] * e.x + pn * e.y);
@@ -210,7 +229,10 @@ hipError_t launch_rope_table(const PrepLaunch &a, float2 *rope, hipStream_t s) {
 
 hipError_t launch_qk_norm_rope(const PrepLaunch &a, hipStream_t s) {
     dim3 grid(a.Lp / kRows, (a.H + kHeads - 1) / kHeads);
-    qk_norm_rope_kernel<<<grid, kThreads, 0, s>>>(a);
+    if (a.F == 16)
+        qk_norm_rope_kernel<16><<<grid, kThreads, 0, s>>>(a);
+    else
+        qk_norm_rope_kernel<8><<<grid, kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 
