@@ -10,8 +10,9 @@
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16.  The A operand is a 32-key slab
 //    of K read from LDS, the B operand Q^T lives in registers for the whole
 //    loop.  In the accumulator every lane then holds ONE query row (lane % 32)
-//    and 16 keys, so the row max / row sum need one cross-half exchange
-//    (v_permlane32_swap) and the O rescale is a per-lane scalar.
+//    and half of the tile's keys, so the row max / row sum need one
+//    cross-half exchange (v_permlane32_swap) and the O rescale is a per-lane
+//    scalar.
 //  * The K slab is read through a row permutation chosen so that accumulator
 //    register 8c+t of lane half h is key 16c + 8h + t: the same registers,
 //    converted to bf16, are the B operand P^T of O^T = V^T P^T with no data
@@ -26,8 +27,11 @@
 //    phase nothing waits on the other unit.
 //  * Softmax in fp32 with exp2 (log2 e folded into the scale) and a lazy
 //    reference max: a row's reference only moves when its max grows by more
-//    than 2^8 (so p <= 256), which makes the O rescale rare.  The row max is
-//    four independent chains of three-input IEEE maximum (NaN-propagating,
+//    than 2^8 (so p <= 256), which makes the O rescale rare.  Each half of a
+//    row first tests its own keys against that threshold; the exchange of
+//    the halves' maxima and the rescale run only in a wave where some row
+//    crossed it (a wave-uniform branch, taken on the first tiles of a work
+//    item and rarely after).  The row max is four independent chains of three-input IEEE maximum (NaN-propagating,
 //    so the raw MFMA results need no canonicalising first) and the row sum
 //    four independent add chains: the softmax wave has no other wave to hide
 //    its latencies behind.
@@ -330,6 +334,9 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
 
         // ---- per-row state: lazy reference max (log2 units), partial row sum, O^T
         float mref = -INFINITY, lsum = 0.f;
+        // mthr: the raw score above which a key's row must move its reference
+        // ((mref + 8) / c2); mu: the reference as the exponent's offset
+        float mthr = -INFINITY, mu = 0.f;
         f32x16 o[4];
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -447,12 +454,21 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
             }
             float mx = __builtin_elementwise_maximum(
                 __builtin_elementwise_maximum(__builtin_elementwise_maximum(m4[0], m4[1]), m4[2]), m4[3]);
-            mx = half_max(mx) * c2;
-            const bool need = mx > mref + 8.0f;
-            const float mnew = need ? mx : mref;
-            const float alpha = need ? __builtin_amdgcn_exp2f(mref - mnew) : 1.0f;
-            mref = mnew;
-            const float mu = (mnew == -INFINITY) ? 0.f : mnew;
+            // each half tests its own 32 keys against the threshold; only a wave
+            // with a row that crossed it exchanges the halves' maxima, moves
+            // those rows' references and rescales their O and row sums
+            if (__ballot(mx > mthr)) {
+                const float mrow = half_max(mx) * c2;
+                const bool need = mrow > mref + 8.0f;
+                const float mnew = need ? mrow : mref;
+                const float alpha = need ? __builtin_amdgcn_exp2f(mref - mnew) : 1.0f;
+                mref = mnew;
+                mu = (mnew == -INFINITY) ? 0.f : mnew;
+                mthr = (mnew + 8.0f) / c2;
+                lsum *= alpha;
+#pragma unroll
+                for (int db = 0; db < 4; ++db) o[db] *= alpha;
+            }
             // probabilities; the row sum (four independent chains, each started
             // by its first pair rather than by adding to zero) is taken over the
             // fp32 values before their rounding to bf16
@@ -473,14 +489,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
                                                  __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
                                                  0, 1, 2, 3, 4, 5, 6, 7);
             }
-            lsum = fmaf(lsum, alpha, (rsp[0] + rsp[1]) + (rsp[2] + rsp[3]));
+            lsum += (rsp[0] + rsp[1]) + (rsp[2] + rsp[3]);
             // keep the softmax in this phase: without a use here the compiler
             // sinks it past the barrier into the MFMA phase that consumes P
             asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3]), "v"(lsum));
-            if (__ballot(need)) {
-#pragma unroll
-                for (int db = 0; db < 4; ++db) o[db] *= alpha;
-            }
         };
 
         // ---- prologue: K(0..2), V(0..1) resident
