@@ -141,6 +141,51 @@ def test_attention_sharpened_logits():
     assert_close(r.out(), ref, "sharpened", max_abs=6e-2)
 
 
+@pytest.mark.parametrize("case", [("L3000_static", 3000, False), ("L12400_queue_split", 12400, True)])
+def test_attention_rising_logits_move_the_reference(case):
+    """Keys turn towards a fixed direction u along the sequence, so the logits
+    of rows aligned with u rise tile by tile: their softmax reference has to
+    move after earlier tiles were accumulated (O and the row sum rescaled
+    mid-sequence), at different tiles for different rows of one wave, while
+    rows orthogonal to u never move it.  u lives in channels 96..127, which
+    RoPE leaves unrotated, so the rise does not depend on positions.  The
+    premise (a rise of more than 8 in log2 units past the first 64 keys of the
+    row's document) is checked on the oracle's Q', K'; the output against the
+    oracle on sampled rows (Q', K' stored in bf16 as the GPU path does), with
+    one item per workgroup and with the work queue and its key-range split."""
+    name, L, split = case
+    rng = np.random.default_rng(70)
+    H = 2
+    lay = synth.random_layout(rng, L, pad_frac=0.05, scattered=False, max_pos=300)
+    u = np.zeros(128)
+    u[96:] = 1.0 / np.sqrt(32.0)
+    a = rng.uniform(0.0, 4.0, size=(L, H, 1))            # a row's alignment with u
+    b = 8.0 * (np.arange(L) / L)[:, None, None]          # keys turn towards u
+    big = np.sqrt(128.0) * u
+    q = synth.f32_to_bf16_bits((rng.standard_normal((L, H, 128)) + a * big).astype(np.float32))
+    k = synth.f32_to_bf16_bits((rng.standard_normal((L, H, 128)) + b * big).astype(np.float32))
+    v = synth.normal_bf16(rng, (L, H, 128))
+    inp = {"q": q, "k": k, "v": v, "layout": lay, "H": H, "D": 128}
+    rows = sample_rows(lay, 160, seed=70)
+    qn = oracle.qk_norm_rope(q[rows], H, 128, 1.0, lay["pos"][rows])
+    kn = oracle.qk_norm_rope(k, H, 128, 1.0, lay["pos"])
+    pad = lay["tags"] == -1
+    c2 = np.log2(np.e) / np.sqrt(128.0)
+    rise = []
+    for i, r in enumerate(rows):
+        keys = np.flatnonzero(pad == pad[r])
+        for h in range(H):
+            sc = (kn[keys, h] @ qn[i, h]) * c2
+            rise.append(sc.max() - sc[:64].max())
+    rise = np.array(rise)
+    say(f"attention rising logits {name}: {np.mean(rise > 8):.2f} of sampled (row, head) rise > 8")
+    assert np.mean(rise > 8) > 0.15 and np.mean(rise < 8) > 0.05
+    r = AttentionRun(inp, split=split).run()
+    ref, lse = _oracle_o(inp, rows=rows, store_qk_bf16=True)
+    assert_close(r.out()[rows], ref, name)
+    assert np.allclose(r.lse_np()[rows], lse, atol=2e-2, rtol=0), "lse"
+
+
 def test_attention_structural():
     import torch
     inp = _random_inputs(31, 900, 2, 0.15)
