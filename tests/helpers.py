@@ -73,7 +73,7 @@ class AttentionRun:
     """Run the attention path through the C ABI on one layout + Q/K/V."""
 
     def __init__(self, inp: dict, wq=None, wk=None, device="cuda", pos_scale=(1.0, 1.0, 1.0),
-                 split=True):
+                 split=True, F=16):
         import torch
         from packed_masked_attention_amd import binding as B
         self.B = B
@@ -83,7 +83,7 @@ class AttentionRun:
         self.H = inp["H"]
         self.D = inp.get("D", 128)
         self.dl = B.pma_layout_build(lay, device=device)
-        self.p = B.attn_params(self.H, pos_scale=pos_scale)
+        self.p = B.attn_params(self.H, F=F, pos_scale=pos_scale)
         self.q = to_dev_bf16(inp["q"], device)
         self.k = to_dev_bf16(inp["k"], device)
         self.v = to_dev_bf16(inp["v"], device)

@@ -28,32 +28,35 @@ def _within_rounding(got, ref, name):
                              f"got {got[i]!r} ref {ref[i]!r}")
 
 
-@pytest.mark.parametrize("case", ["tiny", "random"])
+@pytest.mark.parametrize("case", ["tiny", "random", "random_F8"])
 def test_qk_norm_rope_matches_oracle(case):
+    """F = 16 (the model's rope_freq_dim) and F = 8, where the rotated channels
+    end at 48 and a channel's RoPE partner sits in the neighbouring lane."""
+    F = 8 if case == "random_F8" else 16
     if case == "tiny":
         inp = synth.make_attention_inputs(synth.workload("tiny_L256"))
         w = None
     else:
-        inp = _random_inputs(5, 777, 3, 0.1)
+        inp = _random_inputs(5 if F == 16 else 7, 777, 3, 0.1)
         w = np.random.default_rng(6).uniform(0.5, 2.0, 128)
     say(f"qk_norm_rope {case}")
-    r = AttentionRun(inp, wq=w, wk=w)
+    r = AttentionRun(inp, wq=w, wk=w, F=F)
     r.prep()
     L, H = r.L, r.H
     lay = inp["layout"]
     wv = 1.0 if w is None else w.astype(np.float32).astype(np.float64)
     for name, dev, src in (("Q", r.qh, inp["q"]), ("K", r.kh, inp["k"])):
         got = bf16_to_np(dev)                       # [H, Lp, D]
-        ref = oracle.qk_norm_rope(src, H, 128, wv, lay["pos"])   # [L, H, D]
+        ref = oracle.qk_norm_rope(src, H, 128, wv, lay["pos"], F=F)   # [L, H, D]
         if w is None:   # unit weights: unit-variance outputs, the absolute bound applies
             assert_close(got[:, :L].transpose(1, 0, 2), ref, f"{name}' (tol)")
         # within one bf16 rounding (half an ulp, <= |x| 2^-8) of the fp64 value,
         # plus fp32 slack for cancellation in the rotation
         g = got[:, :L].transpose(1, 0, 2)
         _within_rounding(g, ref, name)
-        # unrotated channels 96..127 are the rounded RMSNorm
-        nrm = oracle.qk_norm_rope(src, H, 128, wv, np.zeros((L, 3), np.int32))
-        _within_rounding(g[..., 96:], nrm[..., 96:], name + " passthrough")
+        # unrotated channels 6F..127 are the rounded RMSNorm
+        nrm = oracle.qk_norm_rope(src, H, 128, wv, np.zeros((L, 3), np.int32), F=F)
+        _within_rounding(g[..., 6 * F:], nrm[..., 6 * F:], name + " passthrough")
         assert np.all(got[:, L:] == 0)
     vt = bf16_to_np(r.vt)                           # [H, D, Lp]
     v = oracle.bf16_to_f64(inp["v"])                # [L, H, D]
@@ -85,6 +88,19 @@ def test_attention_full_parity(case):
     ref, lse = _oracle_o(inp)
     assert_close(r.out(), ref, name)
     assert np.allclose(r.lse_np(), lse, atol=2e-2, rtol=0), "lse"
+
+
+def test_attention_rope_freq_dim_8():
+    """The whole path with F = 8 frequencies per axis (48 rotated channels)
+    against the oracle with the same F; F must change the result."""
+    inp = _random_inputs(16, 1000, 2, 0.1)
+    say("attention rope_freq_dim 8")
+    r = AttentionRun(inp, F=8).run()
+    ref, lse = oracle.attention_path(inp["q"], inp["k"], inp["v"], inp["layout"], 2, F=8)
+    assert_close(r.out(), ref, "F=8")
+    assert np.allclose(r.lse_np(), lse, atol=2e-2, rtol=0), "lse"
+    plain, _ = _oracle_o(inp)
+    assert np.abs(plain - ref).max() > 0.05
 
 
 def test_attention_preview_grid_halved_spatial_rope():
