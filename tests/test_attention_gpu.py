@@ -255,6 +255,37 @@ def test_attention_one_call_entry_point():
     assert torch.equal(o2.view(torch.int16), r.o.view(torch.int16))
 
 
+def test_attention_call_options():
+    """lse = NULL leaves O unchanged; an output row stride wider than H*128
+    writes the same rows and leaves the extra columns alone; an explicit
+    softmax scale s matches the oracle with QK-norm weights w, w^2 = s*sqrt(128)
+    (the logit is (w q_n).(w k_n)/sqrt(128) = s q_n.k_n either way)."""
+    import torch
+    from packed_masked_attention_amd import binding as B
+    inp = _random_inputs(55, 1100, 2, 0.1)
+    L, H = 1100, 2
+    HD = H * 128
+    say("attention call options: lse NULL, wide output stride, explicit scale")
+    r = AttentionRun(inp).run()
+    o_nolse = torch.full_like(r.o, float("nan"))
+    B.pma_flash_attention(r.p, r.dl, r.qh, r.kh, r.vt, o_nolse, HD, None, workspace=r.ws)
+    wide = torch.full((L, HD + 72), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.pma_flash_attention(r.p, r.dl, r.qh, r.kh, r.vt, wide, HD + 72, None, workspace=r.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o_nolse.view(torch.int16), r.o.view(torch.int16)), "lse NULL"
+    assert torch.equal(wide[:, :HD].contiguous().view(torch.int16), r.o.view(torch.int16)), "stride"
+    assert torch.isnan(wide[:, HD:].float()).all(), "columns past H*128 written"
+    sc = 0.05
+    rs = AttentionRun(inp)
+    rs.p = B.attn_params(H, scale=sc)
+    rs.run()
+    w = float(np.sqrt(sc * np.sqrt(128.0)))
+    ref, lse = _oracle_o(inp, w=w)
+    assert_close(rs.out(), ref, "explicit scale")
+    assert np.allclose(rs.lse_np(), lse, atol=2e-2, rtol=0), "lse"
+    assert np.abs(ref - r.out()).max() > 0.05   # the scale changes the result
+
+
 @pytest.mark.parametrize("case", [
     ("L12300_tail_pad", (61, 12300, 2, 12 / 12300, False)),
     ("L13000_scattered", (62, 13000, 3, 0.15, True)),
