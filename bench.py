@@ -55,8 +55,17 @@ def log(*a):
 
 
 def source_hash(path: str) -> str:
+    """16 hex digits of the sha256 of a kernel source plus the extra compiler
+    options the build gives that file, so counters taken on other code (a
+    different source or different code generation) do not apply."""
+    from packed_masked_attention_amd.build import EXTRA
+    h = hashlib.sha256()
     with open(path, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+        h.update(fh.read())
+    opts = EXTRA.get(os.path.basename(path))
+    if opts:
+        h.update(" ".join(opts).encode())
+    return h.hexdigest()[:16]
 
 
 def gpu_state():

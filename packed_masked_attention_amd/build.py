@@ -23,6 +23,13 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-I", os.path.j
           "-Wall", "-Wno-unused-command-line-argument"]
 
 
+# Per-source options.  flash_fwd.hip: LLVM's max-ILP machine scheduler orders
+# the softmax and the fragment reads between the pinned MFMA/DMA groups better
+# than the default occupancy-driven one (same registers, no spills; measured
+# 1-4% faster at 4096-32768 keys).
+EXTRA = {"flash_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith(".hip") or f.endswith(".cpp"))
@@ -31,7 +38,8 @@ def sources():
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"]
-    subprocess.run([HIPCC, *COMMON, *lang, "-c", src, "-o", obj], check=True)
+    extra = EXTRA.get(os.path.basename(src), [])
+    subprocess.run([HIPCC, *COMMON, *extra, *lang, "-c", src, "-o", obj], check=True)
     return obj
 
 
