@@ -97,6 +97,69 @@ def gpu_state():
     return None
 
 
+class ClockSampler:
+    """Samples the card's current sclk level and power from sysfs in a
+    background thread while the timed loop runs (sysfs reads only, no GPU
+    call), so the fraction of peak can also be stated at the clock the card
+    actually ran at.  Every sample is kept; the median is reported."""
+
+    def __init__(self, period_s: float = 0.01):
+        import threading
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._th = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set():
+            st = gpu_state()
+            if st:
+                self.samples.append(st)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        self._th.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._th.join()
+
+    def summary(self):
+        import numpy as np
+        sc = [s["sclk_mhz"] for s in self.samples if "sclk_mhz" in s]
+        pw = [s["power_w"] for s in self.samples if "power_w" in s]
+        if not sc:
+            return None
+        return {"samples": len(sc), "sclk_mhz_median": float(np.median(sc)),
+                "sclk_mhz_range": [float(min(sc)), float(max(sc))],
+                "power_w_median": float(np.median(pw)) if pw else None}
+
+
+def cpu_model() -> str | None:
+    """The host CPU's model name from /proc/cpuinfo (no child process)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+NOMINAL_SCLK_MHZ = 2400.0
+
+
+def at_clock(achieved: float, clock) -> dict | None:
+    """Fraction of the bf16 peak scaled to the sampled median clock."""
+    if not clock:
+        return None
+    peak = BF16_PEAK_TFLOPS * clock["sclk_mhz_median"] / NOMINAL_SCLK_MHZ
+    return {"sclk_mhz": clock["sclk_mhz_median"], "peak": round(peak, 1),
+            "frac": round(achieved / peak, 4)}
+
+
 def attention_flops(tags, H: int, D: int) -> int:
     import numpy as np
     tags = np.asarray(tags)
@@ -147,7 +210,7 @@ def cpu_baseline(inp: dict, target_s: float = 12.0) -> dict:
     t_attn = time.perf_counter() - t0
     flops = 4 * H * D * int(n_doc[rows].sum())
     return {"value": flops / t_attn / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"fp32 two-pass attention for {n} random query rows x {H} heads of "
                       f"the L={L} workload ({t_attn:.1f} s); QK-norm+RoPE of all rows "
                       f"took {t_prep:.1f} s and is not in the rate"}
@@ -183,7 +246,7 @@ def block_cpu_baseline(inp: dict, target_s: float = 12.0) -> dict:
     if dt < target_s / 2:
         n, dt, fl = run(int(min(L, 16 * max(1.0, target_s / max(dt, 1e-3)))))
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"fp64 block for {n} random query rows of the L={L} workload ({dt:.1f} s), "
                       f"including the K/V projection of all {L} rows the attention needs"}
 
@@ -216,7 +279,7 @@ def io_cpu_baseline(d: dict, lay: dict, target_s: float = 10.0) -> dict:
     if dt < target_s / 2:
         n, dt, fl = run(int(256 * max(1.0, (target_s - dt0) / max(dt, 1e-3))))
     return {"value": (fl0 + fl) / (dt0 + dt) / 1e12, "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"fp64 timestep MLP + head table ({dt0:.1f} s) and the video projection + "
                       f"video head for {n} random video rows ({dt:.1f} s)"}
 
@@ -691,18 +754,20 @@ def main() -> int:
     log(f"[bench] timing {args.steps} steps")
     state_before = gpu_state()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     state_after = gpu_state()
+    clock = clk.summary()
     ms_step = wall * 1e3 / args.steps
     per_launch = np.array([a.elapsed_time(b) for a, b in evs])
     flash_ms = float(per_launch.mean())
     q25, q50, q75 = (float(x) for x in np.percentile(per_launch, [25, 50, 75]))
     log(f"[bench] flash per launch: median {q50:.4f} ms, IQR {q25:.4f}-{q75:.4f} ms; "
-        f"gpu before {state_before}, after {state_after}")
+        f"gpu before {state_before}, after {state_after}, during {clock}")
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (flash_ms * 1e-3) / 1e12
 
@@ -738,9 +803,10 @@ def main() -> int:
                      "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic_from_profiles(), "avg_ms": round(flash_ms, 4),
-                     "median_ms": round(q50, 4), "iqr_ms": [round(q25, 4), round(q75, 4)]},
+                     "median_ms": round(q50, 4), "iqr_ms": [round(q25, 4), round(q75, 4)],
+                     "at_measured_clock": at_clock(achieved, clock)},
         "cpu_baseline": cpu,
-        "gpu_state": {"before": state_before, "after": state_after},
+        "gpu_state": {"before": state_before, "after": state_after, "during": clock},
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -354,3 +354,107 @@ def test_attention_work_queue_graph_replays():
         assert torch.equal(r.o.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
         other.flash()                   # eager work on another workspace between replays
         torch.cuda.synchronize()
+
+
+# ------------------------------------------- positions over the whole range
+
+_PMAX = (1 << 24) - 1      # the layout accepts |p| < 2^24
+
+
+def _big_position_inputs(seed, L, H, pad_frac=0.1):
+    """Random layout whose positions span the accepted range: uniform over
+    [-(2^24 - 1), 2^24 - 1] plus rows at both extremes and near zero."""
+    rng = np.random.default_rng(seed)
+    lay = synth.random_layout(rng, L, pad_frac=pad_frac, scattered=True, max_pos=2)
+    pos = rng.integers(-_PMAX, _PMAX + 1, size=(L, 3)).astype(np.int32)
+    pos[:6] = [[_PMAX, _PMAX, _PMAX], [-_PMAX, -_PMAX, -_PMAX], [_PMAX, -_PMAX, 0],
+               [0, 1, -1], [_PMAX - 1, 3, -_PMAX + 1], [1 << 23, -(1 << 23), 12345]]
+    lay = synth.layout_from_tags(lay["tags"], pos, lay["ts_idx"], lay["T"])
+    q, k, v = (synth.normal_bf16(rng, (L, H, 128)) for _ in range(3))
+    return {"q": q, "k": k, "v": v, "layout": lay, "H": H, "D": 128}
+
+
+def test_qk_norm_rope_large_positions():
+    """Angles up to (2^24 - 1) rad: the prep kernel's fp64 angles and cos/sin
+    keep every Q', K' element within one bf16 rounding of the fp64 oracle."""
+    inp = _big_position_inputs(70, 650, 3)
+    w = np.random.default_rng(71).uniform(0.5, 2.0, 128)
+    say("qk_norm_rope at positions up to +-(2^24-1)")
+    r = AttentionRun(inp, wq=w, wk=w)
+    r.prep()
+    lay = inp["layout"]
+    wv = w.astype(np.float32).astype(np.float64)
+    for name, dev, src in (("Q", r.qh, inp["q"]), ("K", r.kh, inp["k"])):
+        got = bf16_to_np(dev)[:, :r.L].transpose(1, 0, 2)
+        ref = oracle.qk_norm_rope(src, r.H, 128, wv, lay["pos"])
+        _within_rounding(got, ref, name + " large positions")
+
+
+@pytest.mark.parametrize("pad_frac", [0.0, 0.15])
+def test_attention_large_positions(pad_frac):
+    inp = _big_position_inputs(72 + int(pad_frac * 100), 1100, 3, pad_frac)
+    say(f"attention at positions up to +-(2^24-1), padding {pad_frac}")
+    r = AttentionRun(inp).run()
+    ref, lse = _oracle_o(inp)
+    assert_close(r.out(), ref, "large positions")
+    assert np.allclose(r.lse_np(), lse, atol=2e-2, rtol=0), "lse"
+
+
+def _gpu_pair_close(a, b, what):
+    """Two GPU results of the same mathematical O (other row order or
+    positions, so other tile maps, summation orders and Q'/K' roundings): per
+    element within 2^-7 of the |v| ~ 1 scale plus the output rounding, far
+    below on average."""
+    assert np.all(np.isfinite(a)) and np.all(np.isfinite(b)), what
+    d = np.abs(a - b)
+    say(f"  {what}: max {d.max():.2e} mean {d.mean():.2e}")
+    assert np.all(d <= 2.0 ** -7 + np.abs(b) * 2.0 ** -7), what
+    assert d.mean() <= 2.5e-4, what
+
+
+@pytest.mark.parametrize("L", [1500, 12400])
+def test_attention_permutation_equivariance(L):
+    """Permuting the rows together with their tags, positions and timestep
+    indices permutes O (the mask is defined by tag, not by position in the
+    sequence).  At 12400 rows the work queue and key-range split run."""
+    H = 2
+    inp = _random_inputs(80 + L % 7, L, H, 0.12, scattered=False)
+    lay = inp["layout"]
+    perm = np.random.default_rng(81).permutation(L)
+    lay_p = synth.layout_from_tags(lay["tags"][perm], lay["pos"][perm], lay["ts_idx"][perm],
+                                   lay["T"])
+    inp_p = {"q": inp["q"][perm], "k": inp["k"][perm], "v": inp["v"][perm], "layout": lay_p,
+             "H": H, "D": 128}
+    say(f"attention permutation equivariance L={L}")
+    a = AttentionRun(inp).run()
+    b = AttentionRun(inp_p).run()
+    rows = sample_rows(lay, 150, seed=82, tile=256)
+    ref, _ = _oracle_o(inp, rows=rows)
+    assert_close(a.out()[rows], ref, "original order")
+    inv = np.argsort(perm)
+    assert_close(b.out()[inv][rows], ref, "permuted, mapped back")
+    _gpu_pair_close(b.out()[inv], a.out(), "permuted vs original")
+    assert np.abs(b.lse_np()[inv] - a.lse_np()).max() < 1e-3
+
+
+@pytest.mark.parametrize("delta", [(1000, -7, 33), (1 << 23, -(1 << 22), 777777)])
+def test_attention_global_position_shift(delta):
+    """Shifting every position by one offset leaves O unchanged (the rotation
+    makes q'.k' depend only on the offset between positions); Q' and K'
+    themselves change, so the GPU results agree within rounding, not bit for
+    bit."""
+    H = 3
+    inp = _random_inputs(90, 1300, H, 0.1)
+    lay = inp["layout"]
+    pos = lay["pos"].astype(np.int64) + np.asarray(delta, np.int64)
+    assert np.abs(pos).max() < (1 << 24)
+    lay_s = synth.layout_from_tags(lay["tags"], pos.astype(np.int32), lay["ts_idx"], lay["T"])
+    say(f"attention global position shift {delta}")
+    a = AttentionRun(inp).run()
+    b = AttentionRun(dict(inp, layout=lay_s)).run()
+    ref, _ = _oracle_o(inp)
+    assert_close(a.out(), ref, "unshifted")
+    assert_close(b.out(), ref, "shifted vs unshifted oracle")
+    _gpu_pair_close(b.out(), a.out(), "shifted vs unshifted")
+    # the Q' of a shifted row does change: the test is not vacuous
+    assert not np.array_equal(bf16_to_np(a.qh), bf16_to_np(b.qh))

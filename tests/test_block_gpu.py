@@ -158,20 +158,28 @@ def test_linear_epilogues_match_numpy(epi, M):
 _one_rounding = one_rounding
 
 
-@pytest.mark.parametrize("F,L,H,hidden,sc", [(16, 700, 4, 512, (1.0, 1.0, 1.0)),
-                                             (8, 300, 2, 256, (1.0, 1.0, 1.0)),
-                                             (16, 500, 2, 256, (1.0, 0.5, 0.5))])
-def test_qkv_projection_matches_oracle(F, L, H, hidden, sc):
+@pytest.mark.parametrize("F,L,H,hidden,sc,pmax", [(16, 700, 4, 512, (1.0, 1.0, 1.0), 300),
+                                                  (8, 300, 2, 256, (1.0, 1.0, 1.0), 300),
+                                                  (16, 500, 2, 256, (1.0, 0.5, 0.5), 300),
+                                                  (16, 600, 2, 256, (1.0, 1.0, 1.0), 1 << 24)])
+def test_qkv_projection_matches_oracle(F, L, H, hidden, sc, pmax):
     """pma_qkv_projection (QKV GEMM with the QK-norm + RoPE epilogue) against
     the oracle's norm and rotation of the fp64 product, and against the
-    unfused GPU path (pma_linear + pma_qk_norm_rope) on the same inputs."""
+    unfused GPU path (pma_linear + pma_qk_norm_rope) on the same inputs.
+    pmax = 2^24: positions over the whole accepted range |p| < 2^24 (angles
+    up to 2^24 - 1 rad), extremes included."""
     import torch
     from packed_masked_attention_amd import binding as B
-    rng = np.random.default_rng(21 + F)
+    rng = np.random.default_rng(21 + F + (pmax > 300))
     tags = rng.integers(0, 3, L).astype(np.int32)
     tags[rng.random(L) < 0.1] = -1
-    pos = rng.integers(0, 300, (L, 3)).astype(np.int32)
-    pos[tags == -1] = 0
+    if pmax > 300:
+        pos = rng.integers(-(pmax - 1), pmax, (L, 3)).astype(np.int32)
+        pos[:3] = [[pmax - 1] * 3, [-(pmax - 1)] * 3, [pmax - 1, -(pmax - 1), 1]]
+        tags[:3] = 0
+    else:
+        pos = rng.integers(0, 300, (L, 3)).astype(np.int32)
+        pos[tags == -1] = 0
     lay = synth.layout_from_tags(tags, pos, np.zeros(L, np.int32), 1)
     HD = H * 128
     a_bits = synth.normal_bf16(rng, (L, hidden))
@@ -235,7 +243,10 @@ def test_block_small_matches_oracle():
     r = BlockRun(inp)
     r.adaln()
     got = r.forward()
-    mod = r.table.cpu().numpy().astype(np.float64)   # same table on both sides
+    # the oracle's own AdaLN table (the GPU's is checked on its own below)
+    mod = oblock.adaln_table(inp["temb"], inp["w_ada"])
+    gmod = r.table.cpu().numpy().astype(np.float64)
+    assert np.allclose(gmod, mod, rtol=1e-5, atol=1e-5 * np.abs(mod).max())
     # an even head count takes the fused QKV projection (Q, K not stored)
     ref = oblock.block_forward(inp, mod=mod, fused_qkv=inp["heads"] % 2 == 0)
     _block_close(got, ref, "block small")
@@ -265,10 +276,11 @@ def test_block_full_size_sampled_rows():
     got = r.forward()
     rows = np.sort(np.random.default_rng(7).choice(wl.L, 24, replace=False))
     say(f"  oracle on {rows.size} sampled rows")
-    mod = r.table.cpu().numpy().astype(np.float64)
+    gmod = r.table.cpu().numpy().astype(np.float64)
     ref_mod = oblock.adaln_table(inp["temb"], inp["w_ada"])
-    assert np.allclose(mod, ref_mod, rtol=1e-4, atol=1e-4 * np.abs(ref_mod).max())
-    ref = oblock.block_forward(inp, rows=rows, mod=mod, fused_qkv=True)
+    assert np.allclose(gmod, ref_mod, rtol=1e-4, atol=1e-4 * np.abs(ref_mod).max())
+    # the end-to-end reference uses the oracle's own table
+    ref = oblock.block_forward(inp, rows=rows, mod=ref_mod, fused_qkv=True)
     _block_close(got[rows], ref, "block L8192 sampled rows")
 
 

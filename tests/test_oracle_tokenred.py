@@ -89,3 +89,48 @@ def test_reduced_stack_with_zero_gates_is_identity():
     dims = {"L": lay["L"], "hidden": hid, "heads": base["heads"], "head_dim": 128, "ffn": base["ffn"]}
     got = ostack.reduced_stack_forward(x, base["temb"], blocks, lay, plan, 1, 2, dims)
     assert np.array_equal(got, x)
+
+
+def _reduced_case(seed0=80):
+    """Three weight sets (non-zero gates) on a small video-heavy layout."""
+    inps = [_tiny_block(seed=seed0 + i, L=96, pad=0) for i in range(3)]
+    base = inps[0]
+    lay = synth.layout_from_counts(16, (2, 4, 8), 16, 0, T=base["layout"]["T"])
+    rng = np.random.default_rng(seed0)
+    x = synth.normal_bf16(rng, (lay["L"], base["hidden"]))
+    blocks = [{k: i[k] for k in _WKEYS} for i in inps]
+    dims = {"L": lay["L"], "hidden": base["hidden"], "heads": base["heads"], "head_dim": 128,
+            "ffn": base["ffn"]}
+    return lay, x, base["temb"], blocks, dims
+
+
+def test_reduced_stack_with_empty_reduced_range_is_the_plain_stack():
+    # merge directly followed by restore: the bypass comes back unchanged
+    # (x + (y - y) is exact), so every block runs at full resolution in order
+    lay, x, temb, blocks, dims = _reduced_case(80)
+    plan = synth.token_reduction_plan(lay)
+    assert (plan["src1"] >= 0).any()
+    full = ostack.stack_forward(x, temb, blocks, lay, dims)
+    for m in (0, 1, 2, 3):
+        got = ostack.reduced_stack_forward(x, temb, blocks, lay, plan, m, m, dims)
+        assert np.array_equal(got, full), m
+    # a non-empty reduced range changes the result (the pin above is not vacuous)
+    red = ostack.reduced_stack_forward(x, temb, blocks, lay, plan, 1, 2, dims)
+    assert not np.array_equal(red, full)
+
+
+def test_reduced_stack_without_pairs_is_the_plain_stack():
+    # a plan that pairs no row (no video row has the target timestep index):
+    # the reduced rows are the full rows, at doubled positions read with
+    # scale 1/2 (exactly the same angles), so the reduced segment is the
+    # plain stack's middle blocks and the restore hands their result back
+    lay, x, temb, blocks, dims = _reduced_case(90)
+    plan = synth.token_reduction_plan(lay, target_ts=lay["T"] + 7)
+    assert (plan["src1"] < 0).all() and np.array_equal(plan["src0"], np.arange(lay["L"]))
+    assert np.array_equal(plan["layout"]["pos"], 2 * lay["pos"])
+    full = ostack.stack_forward(x, temb, blocks, lay, dims)
+    for m, r in ((0, 3), (1, 2), (1, 3), (0, 1)):
+        got = ostack.reduced_stack_forward(x, temb, blocks, lay, plan, m, r, dims)
+        assert np.array_equal(got, full), (m, r)
+    # an off-by-one in the block ranges would run a block twice or skip one
+    assert not np.array_equal(ostack.stack_forward(x, temb, blocks[:2], lay, dims), full)
