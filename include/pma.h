@@ -222,6 +222,26 @@ pma_status pma_flash_attention(const pma_attn_params *p, const pma_layout *layou
                                pma_bf16 *o, int64_t o_ld, float *lse, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* Allocation-free form of pma_flash_attention, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, checks and results
+ * contract as pma_flash_attention, without the workspace: the work-queue
+ * counters and the split items' partial results live in a file-scope device
+ * array of PMA_FLASH_STATIC_SCRATCH_BYTES (32 MiB) that every GPU the library
+ * runs on holds until the process ends.  The array bounds the key-range
+ * split to the items it holds: up to 7 split items per XCD (the workspace
+ * form takes up to 16), so from 12288 keys on the two forms agree to fp32
+ * rounding order, and below that bit for bit.  No shape is refused for the
+ * array's size.  The call allocates nothing; the counters are cleared by a
+ * kernel on the stream at every call.  All calls on one GPU share its array:
+ * calls that overlap on one GPU (other streams, other threads) race and must
+ * not be issued. */
+#define PMA_FLASH_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+pma_status pma_flash_attention_static(const pma_attn_params *p, const pma_layout *layout,
+                                      const pma_bf16 *qh, const pma_bf16 *kh,
+                                      const pma_bf16 *vt, pma_bf16 *o, int64_t o_ld, float *lse,
+                                      void *stream);
+
 /* Workspace of pma_attention: qh, kh and vt (3 * H * Lp * D bf16), then the
  * flash workspace (pma_flash_workspace_size). */
 pma_status pma_attention_workspace_size(const pma_attn_params *p, int32_t seq_len,

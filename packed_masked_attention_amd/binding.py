@@ -101,6 +101,8 @@ _SIGS = {
                                         ctypes.POINTER(ctypes.c_size_t)]),
     "pma_flash_attention": (_i32, [ctypes.POINTER(AttnParams), ctypes.POINTER(Layout), _vp, _vp,
                                    _vp, _vp, _i64, _vp, _vp, ctypes.c_size_t, _vp]),
+    "pma_flash_attention_static": (_i32, [ctypes.POINTER(AttnParams), ctypes.POINTER(Layout), _vp,
+                                          _vp, _vp, _vp, _i64, _vp, _vp]),
     "pma_attention_workspace_size": (_i32, [ctypes.POINTER(AttnParams), _i32,
                                             ctypes.POINTER(ctypes.c_size_t)]),
     "pma_attention": (_i32, [ctypes.POINTER(AttnParams), ctypes.POINTER(Layout), _vp, _i64, _vp,
@@ -317,6 +319,15 @@ def pma_flash_attention(p: AttnParams, dl: DeviceLayout, qh, kh, vt, o, o_ld, ls
     check(lib().pma_flash_attention(ctypes.byref(p), ctypes.byref(dl.struct), ptr(qh), ptr(kh),
                                     ptr(vt), ptr(o), o_ld, ptr(lse), ptr(workspace), nbytes,
                                     stream_ptr(stream)))
+
+
+def pma_flash_attention_static(p: AttnParams, dl: DeviceLayout, qh, kh, vt, o, o_ld, lse=None,
+                               stream=None) -> None:
+    """pma_flash_attention without a workspace: its scratch is the library's
+    static device array (allocates nothing; overlapping calls on one GPU race)."""
+    check(lib().pma_flash_attention_static(ctypes.byref(p), ctypes.byref(dl.struct), ptr(qh),
+                                           ptr(kh), ptr(vt), ptr(o), o_ld, ptr(lse),
+                                           stream_ptr(stream)))
 
 
 def pma_attention_workspace_size(p: AttnParams, seq_len: int) -> int:

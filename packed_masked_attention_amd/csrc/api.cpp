@@ -307,10 +307,14 @@ pma_status pma_flash_workspace_size(const pma_attn_params *p, int32_t seq_len, s
     return PMA_OK;
 }
 
-pma_status pma_flash_attention(const pma_attn_params *p, const pma_layout *layout,
-                               const pma_bf16 *qh, const pma_bf16 *kh, const pma_bf16 *vt,
-                               pma_bf16 *o, int64_t o_ld, float *lse, void *workspace,
-                               size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the two flash entry points.
+pma_status check_flash_args(const pma_attn_params *p, const pma_layout *layout,
+                            const pma_bf16 *qh, const pma_bf16 *kh, const pma_bf16 *vt,
+                            pma_bf16 *o, int64_t o_ld, float *lse) {
     pma_status st;
     if ((st = check_attn_params(p)) != PMA_OK) return st;
     if ((st = check_layout(layout)) != PMA_OK) return st;
@@ -327,15 +331,14 @@ pma_status pma_flash_attention(const pma_attn_params *p, const pma_layout *layou
         return fail(PMA_ERR_ALIGN, "qh, kh, vt must be 16-byte aligned");
     if ((st = check_tok_major("o", o, o_ld, p->num_heads)) != PMA_OK) return st;
     if (lse && !aligned(lse, 4)) return fail(PMA_ERR_ALIGN, "lse must be 4-byte aligned");
-    if (workspace) {
-        size_t need = 0;
-        if ((st = pma_flash_workspace_size(p, layout->seq_len, &need)) != PMA_OK) return st;
-        if (!aligned(workspace, 256)) return fail(PMA_ERR_ALIGN, "workspace must be 256-byte aligned");
-        if (workspace_bytes < need)
-            return fail(PMA_ERR_WORKSPACE, "flash workspace %zu < %zu bytes", workspace_bytes, need);
-    }
-    if ((st = check_device()) != PMA_OK) return st;
+    return PMA_OK;
+}
 
+// Launch with split_items split items per XCD (0: one item per workgroup,
+// no work queue); ws holds flash_split_bytes_for(split_items) bytes.
+pma_status flash_launch(const pma_attn_params *p, const pma_layout *layout, const pma_bf16 *qh,
+                        const pma_bf16 *kh, const pma_bf16 *vt, pma_bf16 *o, int64_t o_ld,
+                        float *lse, void *ws, int32_t split_items, void *stream) {
     const float scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)kHeadDim);
     FlashLaunch a;
     a.L = layout->seq_len;
@@ -352,14 +355,80 @@ pma_status pma_flash_attention(const pma_attn_params *p, const pma_layout *layou
     a.count = layout->tile_count;
     a.list = layout->tile_list;
     a.order = layout->tile_order;
-    // the work queue pays off on long key lists only (see flash_split_items)
-    a.split_items = workspace ? flash_split_items(a.H, a.L) : 0;
-    a.queue = a.split_items > 0 ? static_cast<int32_t *>(workspace) : nullptr;
-    a.part = a.split_items > 0
-                 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + kFlashQueueBytes)
-                 : nullptr;
+    a.split_items = split_items;
+    a.queue = split_items > 0 ? static_cast<int32_t *>(ws) : nullptr;
+    a.part = split_items > 0 ? reinterpret_cast<float *>(static_cast<char *>(ws) + kFlashQueueBytes)
+                             : nullptr;
     PMA_CHECK_HIP(launch_flash_attention(a, static_cast<hipStream_t>(stream)), "flash launch");
     return PMA_OK;
+}
+
+// ---- scratch of the allocation-free entry point.  A file-scope device
+// array: every GPU the library runs on holds its own copy (at its own
+// address) until the process ends.  Host code never uses the array's name
+// as an address: the device address is fetched once per device with
+// hipGetSymbolAddress and kept in g_scratch.
+constexpr size_t kScratchBytes = PMA_FLASH_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch[64];
+
+pma_status scratch_address(void **out) {
+    int dev = 0;
+    PMA_CHECK_HIP(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(PMA_ERR_UNSUPPORTED, "device index %d", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        PMA_CHECK_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(PMA_ERR_DEVICE, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return PMA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pma_status pma_flash_attention(const pma_attn_params *p, const pma_layout *layout,
+                               const pma_bf16 *qh, const pma_bf16 *kh, const pma_bf16 *vt,
+                               pma_bf16 *o, int64_t o_ld, float *lse, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    pma_status st;
+    if ((st = check_flash_args(p, layout, qh, kh, vt, o, o_ld, lse)) != PMA_OK) return st;
+    if (workspace) {
+        size_t need = 0;
+        if ((st = pma_flash_workspace_size(p, layout->seq_len, &need)) != PMA_OK) return st;
+        if (!aligned(workspace, 256)) return fail(PMA_ERR_ALIGN, "workspace must be 256-byte aligned");
+        if (workspace_bytes < need)
+            return fail(PMA_ERR_WORKSPACE, "flash workspace %zu < %zu bytes", workspace_bytes, need);
+    }
+    if ((st = check_device()) != PMA_OK) return st;
+    // the work queue pays off on long key lists only (see flash_split_items)
+    const int32_t split = workspace ? flash_split_items(p->num_heads, layout->seq_len) : 0;
+    return flash_launch(p, layout, qh, kh, vt, o, o_ld, lse, workspace, split, stream);
+}
+
+pma_status pma_flash_attention_static(const pma_attn_params *p, const pma_layout *layout,
+                                      const pma_bf16 *qh, const pma_bf16 *kh, const pma_bf16 *vt,
+                                      pma_bf16 *o, int64_t o_ld, float *lse, void *stream) {
+    pma_status st;
+    if ((st = check_flash_args(p, layout, qh, kh, vt, o, o_ld, lse)) != PMA_OK) return st;
+    if ((st = check_device()) != PMA_OK) return st;
+    // as many split items per XCD as the workspace form would take, up to
+    // what the array holds
+    int32_t split = flash_split_items(p->num_heads, layout->seq_len);
+    while (split > 0 && flash_split_bytes_for(split) > kScratchBytes) --split;
+    const size_t need = flash_split_bytes_for(split);
+    if (need > kScratchBytes)
+        return fail(PMA_ERR_WORKSPACE, "flash scratch needs %zu bytes, the static array holds %zu",
+                    need, kScratchBytes);
+    void *ws = nullptr;
+    if ((st = scratch_address(&ws)) != PMA_OK) return st;
+    return flash_launch(p, layout, qh, kh, vt, o, o_ld, lse, ws, split, stream);
 }
 
 pma_status pma_attention_workspace_size(const pma_attn_params *p, int32_t seq_len,

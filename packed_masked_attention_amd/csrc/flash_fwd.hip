@@ -670,9 +670,11 @@ int32_t flash_split_items(int32_t H, int32_t L) {
     return per_xcd < kSplitItems ? per_xcd : kSplitItems;
 }
 
-size_t flash_split_bytes(int32_t H, int32_t L) {
-    return kFlashQueueBytes + (size_t)8 * flash_split_items(H, L) * kSplitParts * kPartFloats * sizeof(float);
+size_t flash_split_bytes_for(int32_t split_items) {
+    return kFlashQueueBytes + (size_t)8 * split_items * kSplitParts * kPartFloats * sizeof(float);
 }
+
+size_t flash_split_bytes(int32_t H, int32_t L) { return flash_split_bytes_for(flash_split_items(H, L)); }
 
 void flash_tiles(int32_t *tile_m, int32_t *tile_n) {
     *tile_m = kBM;

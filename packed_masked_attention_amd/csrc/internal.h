@@ -86,6 +86,8 @@ constexpr size_t kFlashQueueBytes = 256;
 // and partial results) the split needs
 int32_t flash_split_items(int32_t H, int32_t L);
 size_t flash_split_bytes(int32_t H, int32_t L);
+// work-queue counters + partial results of split_items split items per XCD
+size_t flash_split_bytes_for(int32_t split_items);
 // most k-tiles a layout may have for the attention kernel (its LDS tile list)
 int32_t flash_max_k_tiles();
 hipError_t launch_flash_attention(const FlashLaunch &a, hipStream_t s);
