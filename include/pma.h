@@ -182,7 +182,11 @@ pma_status pma_attention_padded_len(int32_t seq_len, int32_t *padded_len);
  *            ld >= H*D, ld % 8 == 0, 16-byte aligned (the QKV projection
  *            output [L][3*H*D] is used with ld = 3*H*D and offsets 0, HD, 2HD).
  *   q_norm_weight, k_norm_weight: fp32 [D], shared by all heads.
- *   qh, kh: bf16 [H][Lp][D] head-major normalised, rotated Q and K.
+ *   qh, kh: bf16 [H][Lp][D] head-major normalised, rotated Q and K.  qh also
+ *           carries the attention's logit factor: it holds the normalised,
+ *           rotated Q times softmax_scale * log2(e) (both in fp32, rounded to
+ *           bf16 once), so the attention kernel's QK product is the softmax
+ *           exponent in base 2.
  *   vt:     bf16 [H][D][Lp] V transposed per head (keys contiguous).
  *   Rows L..Lp-1 of qh, kh and columns L..Lp-1 of vt are written as zero.
  * [ENG] "Checkpoint layout en media pipeline" fuses the QK norm with RoPE;
@@ -195,10 +199,16 @@ pma_status pma_qk_norm_rope(const pma_attn_params *p, const pma_layout *layout,
 
 /* Bytes of the optional workspace of pma_flash_attention: 256 bytes of
  * work-queue counters, then the partial results of the items whose key
- * ranges are split (none below 12288 keys). */
+ * ranges are split (none below 12288 keys), then (when any item is split)
+ * 32 KiB of clock stamps: for each persistent workgroup of the last call
+ * (at most 1024, one per CU), four u64 -- the shader clock counter and the
+ * 100 MHz real-time counter at its start, the same two at its end -- from
+ * which a caller can read the clock the kernel ran at. */
 pma_status pma_flash_workspace_size(const pma_attn_params *p, int32_t seq_len, size_t *bytes);
 
-/* Masked flash attention forward on the operands of pma_qk_norm_rope.
+/* Masked flash attention forward on the operands of pma_qk_norm_rope (or
+ * pma_qkv_projection): the logit of query i and key j is qh[i].kh[j] in base
+ * 2, i.e. the softmax scale is the one qh was produced with.
  * layout must be built with pma_attention_tiles()' tiling.  Tiles the layout
  * marks EMPTY are skipped whole; PARTIAL tiles and the ragged last k-tile
  * apply the document/bounds mask.
@@ -353,7 +363,9 @@ pma_status pma_rope_table(const pma_attn_params *p, const pma_layout *layout, fl
  * then K, then V) it writes the operands pma_qk_norm_rope would write --
  * qh, kh [H][Lp][D] normalised and rotated, vt [H][D][Lp] -- without storing
  * Q, K, V: the norm and rotation read the fp32 accumulators (Q and K are
- * rounded to bf16 once, after rotation).  Rows L..Lp-1 are written as zero.
+ * rounded to bf16 once, after rotation; qh carries the logit factor
+ * softmax_scale * log2(e) as in pma_qk_norm_rope).  Rows L..Lp-1 are written
+ * as zero.
  * H must be even (a 256-column tile never straddles Q, K and V); hidden %
  * 64 == 0; a, w_qkv, qh, kh, vt, the norm weights and rope_table (from
  * pma_rope_table) 16-byte aligned.

@@ -116,6 +116,14 @@ def bf16_storage(x: np.ndarray) -> np.ndarray:
     return bf16_to_f64(bf16_round(x))
 
 
+def stored_query(qn: np.ndarray, D: int = 128) -> np.ndarray:
+    """Normalised, rotated queries as the GPU path stores them: rounded to bf16
+    after multiplication by log2(e)/sqrt(D) (its attention kernel takes exp2 of
+    the raw product), returned with that factor divided out in fp64."""
+    c = np.log2(np.e) / np.sqrt(D)
+    return bf16_storage(qn * c) / c
+
+
 # -------------------------------------------------------------- layout ----
 
 def layout_status(layout: dict) -> tuple[int, int]:
@@ -216,16 +224,18 @@ def attention_path(q_bits, k_bits, v_bits, layout: dict, H: int, D: int = 128,
     """QK-RMSNorm + 3-axis RoPE on Q and K, then masked attention.
 
     Inputs are bf16 bit arrays [L, H, D] (or [L, ld] with head h at column h*D).
-    ``store_qk_bf16`` rounds the normalised, rotated Q and K to bf16 (the
-    tensors the GPU path stores between its two kernels); otherwise the path
-    stays in fp64 end to end.
+    ``store_qk_bf16`` rounds the normalised, rotated Q and K to bf16 as the
+    GPU path stores them between its two kernels: K as it is, Q multiplied by
+    the logit factor log2(e)/sqrt(D) (the stored query operand carries the
+    softmax scale and the base change to exp2), the factor then divided out
+    in fp64.  Otherwise the path stays in fp64 end to end.
     """
     L = np.asarray(q_bits).shape[0]
     pos = layout["pos"]
     qn = qk_norm_rope(q_bits, H, D, wq, pos, F, theta, eps, pos_scale)
     kn = qk_norm_rope(k_bits, H, D, wk, pos, F, theta, eps, pos_scale)
     if store_qk_bf16:
-        qn = bf16_storage(qn)
+        qn = stored_query(qn, D)
         kn = bf16_storage(kn)
     vv = bf16_to_f64(np.ascontiguousarray(v_bits).reshape(L, -1)[:, :H * D]).reshape(L, H, D)
     return attention(qn, kn, vv, layout["tags"], rows=rows, precision=precision)

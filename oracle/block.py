@@ -21,13 +21,14 @@ Readings (listed in DESIGN.md):
 Weights are [out, in]: y = u @ W.T.
 
 ``store_bf16=True`` rounds to bf16 exactly the tensors the GPU path stores
-(a, Q, K, V, normalised Q and K, O, x1, b, h, x2); every other value is fp64.
+(a, Q, K, V, normalised Q and K, O, x1, b, h, x2; the normalised Q is stored
+times log2(e)/sqrt(D), see stored_query); every other value is fp64.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from . import attention, bf16_storage, bf16_to_f64, qk_norm_rope
+from . import attention, bf16_storage, bf16_to_f64, qk_norm_rope, stored_query
 
 SHIFT_A, SCALE_A, GATE_A, SHIFT_F, SCALE_F, GATE_F = range(6)
 
@@ -108,7 +109,7 @@ def block_forward(inp: dict, rows=None, store_bf16: bool = True, eps: float = 1e
     qn = qk_norm_rope(q_all, H, D, wq, lay["pos"], F, theta, qk_eps, pos_scale)
     kn = qk_norm_rope(kv[:, :HD], H, D, wk, lay["pos"], F, theta, qk_eps, pos_scale)
     if store_bf16:
-        qn, kn = bf16_storage(qn), bf16_storage(kn)
+        qn, kn = stored_query(qn, D), bf16_storage(kn)
     v = kv[:, HD:].reshape(L, H, D)
     o, _ = attention(qn, kn, v, tags, rows=rows)
     o = st(o.reshape(rows.size, HD))

@@ -138,6 +138,13 @@ void api_fill_rope(const pma_attn_params *p, PrepLaunch &a) {
     for (int ax = 0; ax < 3; ++ax)
         a.pos_scale[ax] = p->pos_scale[ax] == 0.f ? 1.0 : (double)p->pos_scale[ax];
 }
+// The attention operand Q' carries the logit scale: Q' = q_normed_rotated *
+// softmax_scale * log2(e), so the attention kernel's scores are log2-unit
+// logits straight out of the MFMA and exp2 applies with no multiply.
+float api_q_operand_scale(const pma_attn_params *p) {
+    const float scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)kHeadDim);
+    return scale * 1.4426950408889634f;
+}
 pma_status api_check_layout(const pma_layout *l) { return check_layout(l); }
 int32_t api_padded_len(int32_t L) { return padded_len(L); }
 }  // namespace pma
@@ -288,6 +295,7 @@ pma_status pma_qk_norm_rope(const pma_attn_params *p, const pma_layout *layout,
     a.H = H;
     a.F = p->rope_freq_dim;
     a.eps = p->qk_norm_eps;
+    a.qscale = api_q_operand_scale(p);
     api_fill_rope(p, a);
     a.q = q; a.k = k; a.v = v;
     a.q_ld = q_ld; a.k_ld = k_ld; a.v_ld = v_ld;
@@ -303,7 +311,9 @@ pma_status pma_flash_workspace_size(const pma_attn_params *p, int32_t seq_len, s
     if ((st = check_attn_params(p)) != PMA_OK) return st;
     if (!bytes) return fail(PMA_ERR_NULL, "bytes is NULL");
     if (seq_len < 1 || seq_len > (1 << 24)) return fail(PMA_ERR_SHAPE, "seq_len %d", seq_len);
-    *bytes = flash_split_bytes(p->num_heads, seq_len);
+    // the clock stamps of the persistent launch follow the partial results
+    *bytes = flash_split_bytes(p->num_heads, seq_len) +
+             (flash_split_items(p->num_heads, seq_len) > 0 ? kFlashStampBytes : 0);
     return PMA_OK;
 }
 
@@ -335,19 +345,17 @@ pma_status check_flash_args(const pma_attn_params *p, const pma_layout *layout,
 }
 
 // Launch with split_items split items per XCD (0: one item per workgroup,
-// no work queue); ws holds flash_split_bytes_for(split_items) bytes.
+// no work queue); ws holds flash_split_bytes_for(split_items) bytes, then
+// (stamps) the clock-stamp area.
 pma_status flash_launch(const pma_attn_params *p, const pma_layout *layout, const pma_bf16 *qh,
                         const pma_bf16 *kh, const pma_bf16 *vt, pma_bf16 *o, int64_t o_ld,
-                        float *lse, void *ws, int32_t split_items, void *stream) {
-    const float scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)kHeadDim);
+                        float *lse, void *ws, int32_t split_items, bool stamps, void *stream) {
     FlashLaunch a;
     a.L = layout->seq_len;
     a.Lp = padded_len(a.L);
     a.H = p->num_heads;
     a.nqt = layout->num_q_tiles;
     a.nkt = layout->num_k_tiles;
-    a.scale = scale;
-    a.scale_log2 = scale * 1.4426950408889634f;
     a.qh = qh; a.kh = kh; a.vt = vt;
     a.o = o; a.o_ld = o_ld; a.lse = lse;
     a.doc = layout->doc;
@@ -359,6 +367,10 @@ pma_status flash_launch(const pma_attn_params *p, const pma_layout *layout, cons
     a.queue = split_items > 0 ? static_cast<int32_t *>(ws) : nullptr;
     a.part = split_items > 0 ? reinterpret_cast<float *>(static_cast<char *>(ws) + kFlashQueueBytes)
                              : nullptr;
+    a.stamps = split_items > 0 && stamps
+                   ? reinterpret_cast<uint64_t *>(static_cast<char *>(ws) +
+                                                  flash_split_bytes_for(split_items))
+                   : nullptr;
     PMA_CHECK_HIP(launch_flash_attention(a, static_cast<hipStream_t>(stream)), "flash launch");
     return PMA_OK;
 }
@@ -409,7 +421,7 @@ pma_status pma_flash_attention(const pma_attn_params *p, const pma_layout *layou
     if ((st = check_device()) != PMA_OK) return st;
     // the work queue pays off on long key lists only (see flash_split_items)
     const int32_t split = workspace ? flash_split_items(p->num_heads, layout->seq_len) : 0;
-    return flash_launch(p, layout, qh, kh, vt, o, o_ld, lse, workspace, split, stream);
+    return flash_launch(p, layout, qh, kh, vt, o, o_ld, lse, workspace, split, true, stream);
 }
 
 pma_status pma_flash_attention_static(const pma_attn_params *p, const pma_layout *layout,
@@ -428,7 +440,7 @@ pma_status pma_flash_attention_static(const pma_attn_params *p, const pma_layout
                     need, kScratchBytes);
     void *ws = nullptr;
     if ((st = scratch_address(&ws)) != PMA_OK) return st;
-    return flash_launch(p, layout, qh, kh, vt, o, o_ld, lse, ws, split, stream);
+    return flash_launch(p, layout, qh, kh, vt, o, o_ld, lse, ws, split, false, stream);
 }
 
 pma_status pma_attention_workspace_size(const pma_attn_params *p, int32_t seq_len,

@@ -19,6 +19,7 @@ pma_status api_check_attn_params(const pma_attn_params *p);
 pma_status api_check_layout(const pma_layout *l);
 int32_t api_padded_len(int32_t L);
 void api_fill_rope(const pma_attn_params *p, PrepLaunch &a);
+float api_q_operand_scale(const pma_attn_params *p);
 }  // namespace pma
 
 namespace {
@@ -188,6 +189,7 @@ pma_status pma_qkv_projection(const pma_attn_params *p, const pma_layout *layout
     g.epi = p->rope_freq_dim == 16 ? kEpiQkvRope : kEpiQkvRope + 1;
     g.Lp = api_padded_len(L); g.H = H; g.F = p->rope_freq_dim;
     g.eps = p->qk_norm_eps;
+    g.qscale = api_q_operand_scale(p);
     g.wq = q_norm_weight; g.wk = k_norm_weight;
     g.rope = reinterpret_cast<const float2 *>(rope_table);
     g.qh = qh; g.kh = kh; g.vt = vt;

@@ -25,9 +25,13 @@
 //    S(t) (VALU only).  While one wave of a SIMD runs its MFMAs the other runs
 //    its softmax, so matrix and vector units work at the same time; within a
 //    phase nothing waits on the other unit.
-//  * Softmax in fp32 with exp2 (log2 e folded into the scale) and a lazy
-//    reference max: a row's reference only moves when its max grows by more
-//    than 2^8 (so p <= 256), which makes the O rescale rare.  Each half of a
+//  * Softmax in fp32 with exp2.  Q' carries the logit scale (softmax_scale *
+//    log2 e, applied where Q' is produced), and the QK accumulators of a row
+//    start from minus its reference instead of zero, so the MFMA delivers
+//    log2-unit logits relative to the reference and p = exp2(s) needs no
+//    per-score arithmetic.  The reference is lazy: it only moves when the
+//    row's max grows by more than 2^8 (so p <= 256), which makes the O
+//    rescale rare (it then also shifts that tile's scores).  Each half of a
 //    row first tests its own keys against that threshold; the exchange of
 //    the halves' maxima and the rescale run only in a wave where some row
 //    crossed it (a wave-uniform branch, taken on the first tiles of a work
@@ -83,8 +87,8 @@ constexpr int kD = kHeadDim;               // 128
 constexpr int kTileElems = kBN * kD;       // 8192 bf16 = 16 KB per K or V^T tile
 constexpr int kKI = 16 / kNW;              // 1 KB LDS-DMA instructions per wave per tile
 constexpr int kNDMA = 2 * kKI + 1;         // DMA instructions per wave per tile (K, V^T, ids)
-constexpr int kReadAhead = 4;              // LDS fragment reads in flight ahead of the MFMAs
-constexpr int kVPre = 4;                   // V fragments read during the softmax phase
+constexpr int kReadAhead = 3;              // LDS fragment reads in flight ahead of the MFMAs
+constexpr int kVPre = 2;                   // V fragments read during the softmax phase
 constexpr int kMask = 0x3fffffff;          // list entry -> k-tile index
 constexpr int kSplitItems = 16;            // items per XCD split over their key range
 constexpr int kSplitMinKeyTiles = 192;     // no split below this many k-tiles (12288 keys)
@@ -230,6 +234,15 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
     const int xcd_hw = (int)(__builtin_amdgcn_s_getreg(20 | (15 << 11)) & 7);
     __shared__ int2 work;
     (void)arg;   // read through the kernarg segment below
+    if (tid == 0) {
+        // clock stamps (persistent launches with a workspace): shader clock
+        // and 100 MHz real-time clock at the workgroup's start
+        uint64_t *st = ((kernarg_launch)__builtin_amdgcn_kernarg_segment_ptr())->stamps;
+        if (st) {
+            st[4 * blockIdx.x] = __builtin_amdgcn_s_memtime();
+            st[4 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+        }
+    }
     for (int iter = 0;; ++iter) {
         // the launch arguments, read again for every item, so that none of them
         // stays live across the work loop
@@ -330,13 +343,17 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
         };
 
         const int krow = k_slab_row(l32);
-        const float c2 = a.scale_log2;
 
-        // ---- per-row state: lazy reference max (log2 units), partial row sum, O^T
+        // ---- per-row state (log2 units): lazy reference max (-inf until the
+        // row's first key), partial row sum, O^T.  mu is the offset the QK
+        // accumulators start from (-mu in every register of sd): the
+        // reference once set, 0 before; thr is the score (relative to mu)
+        // above which the row must move its reference: 8 once set, -inf before.
         float mref = -INFINITY, lsum = 0.f;
-        // mthr: the raw score above which a key's row must move its reference
-        // ((mref + 8) / c2); mu: the reference as the exponent's offset
-        float mthr = -INFINITY, mu = 0.f;
+        float thr = -INFINITY, mu = 0.f;
+        f32x16 sd;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sd[v] = 0.f;
         f32x16 o[4];
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -346,7 +363,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
         bf16x8 pf[4];    // P(t)^T in bf16, 4 chunks of 16 keys
         bf16x8 vpre[kVPre];
 
-        // ---- MFMA phase: O^T += V(t-1)^T P(t-1)^T (when withpv), S(t) = K(t) Q^T
+        // ---- MFMA phase: O^T += V(t-1)^T P(t-1)^T (when withpv), S(t) = K(t) Q^T - mu
         auto gphase = [&](bool withpv, const uint16_t *vr, const uint16_t *kr, int dk, uint16_t *dks,
                           int dv, uint16_t *dvs) __attribute__((always_inline)) {
             // the document-id DMA (8 lanes) ahead of the scheduled region: its
@@ -380,17 +397,15 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
                     }
             }
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
-#pragma unroll
             for (int c = 0; c < 8; ++c)
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     const int r = 32 * kb + krow;
                     const bf16x8 kf =
                         *reinterpret_cast<const bf16x8 *>(kr + r * kD + 8 * k_pos(r, 2 * c + hi));
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
+                    // the first k-step starts from the seed -mu
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], c == 0 ? sd : s[kb],
+                                                                    0, 0, 0);
                     if (withpv && c == 2 && kb == 1) dma_v1(dv, dvs, 1);
                 }
             // LDS fragment reads run kReadAhead ahead of their MFMAs; the DMA
@@ -456,18 +471,26 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
                 __builtin_elementwise_maximum(__builtin_elementwise_maximum(m4[0], m4[1]), m4[2]), m4[3]);
             // each half tests its own 32 keys against the threshold; only a wave
             // with a row that crossed it exchanges the halves' maxima, moves
-            // those rows' references and rescales their O and row sums
-            if (__ballot(mx > mthr)) {
-                const float mrow = half_max(mx) * c2;
-                const bool need = mrow > mref + 8.0f;
-                const float mnew = need ? mrow : mref;
+            // those rows' references, rescales their O and row sums and shifts
+            // this tile's scores to the new reference
+            if (__ballot(mx > thr)) {
+                const float mrow = half_max(mx);           // relative to mu
+                const bool need = mrow > thr;
+                const float shift = need ? mrow : 0.f;
+                const float mnew = need ? mu + mrow : mref;
                 const float alpha = need ? __builtin_amdgcn_exp2f(mref - mnew) : 1.0f;
                 mref = mnew;
-                mu = (mnew == -INFINITY) ? 0.f : mnew;
-                mthr = (mnew + 8.0f) / c2;
+                mu = need ? mnew : mu;
+                thr = (mref - mu) + 8.0f;
                 lsum *= alpha;
 #pragma unroll
                 for (int db = 0; db < 4; ++db) o[db] *= alpha;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) s[kb][v] -= shift;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) sd[v] = -mu;
             }
             // probabilities; the row sum (four independent chains, each started
             // by its first pair rather than by adding to zero) is taken over the
@@ -478,9 +501,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
                 bf16x2 pp[4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[cc >> 1][8 * (cc & 1) + 2 * t], c2, -mu));
-                    const float p1 =
-                        __builtin_amdgcn_exp2f(fmaf(s[cc >> 1][8 * (cc & 1) + 2 * t + 1], c2, -mu));
+                    const float p0 = __builtin_amdgcn_exp2f(s[cc >> 1][8 * (cc & 1) + 2 * t]);
+                    const float p1 = __builtin_amdgcn_exp2f(s[cc >> 1][8 * (cc & 1) + 2 * t + 1]);
                     const f32x2 pv = {p0, p1};
                     pp[t] = __builtin_convertvector(pv, bf16x2);
                     rsp[t] = cc ? rsp[t] + (p0 + p1) : p0 + p1;
@@ -607,6 +629,13 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
                 a.lse[(int64_t)head * a.L + qrow] = (mref + __log2f(lt)) * 0.69314718055994531f;
         }
     }   // work loop
+    if (tid == 0) {
+        uint64_t *st = ((kernarg_launch)__builtin_amdgcn_kernarg_segment_ptr())->stamps;
+        if (st) {
+            st[4 * blockIdx.x + 2] = __builtin_amdgcn_s_memtime();
+            st[4 * blockIdx.x + 3] = __builtin_amdgcn_s_memrealtime();
+        }
+    }
 }
 
 // Zero the work-queue counters (a kernel rather than a memset, so the
@@ -696,8 +725,10 @@ hipError_t launch_flash_attention(const FlashLaunch &a, hipStream_t s) {
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
+    FlashLaunch b = a;
+    if (cus > kFlashStampGroups) b.stamps = nullptr;
     flash_queue_reset_kernel<<<1, 64, 0, s>>>(a.queue);
-    flash_fwd_kernel<<<cus, kNW * 64, dyn, s>>>(a);
+    flash_fwd_kernel<<<cus, kNW * 64, dyn, s>>>(b);
     if (a.split_items > 0) flash_merge_kernel<<<8 * a.split_items * (kBM / 8), 256, 0, s>>>(a);
     return hipGetLastError();
 }

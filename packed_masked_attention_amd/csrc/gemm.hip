@@ -14,7 +14,9 @@
 //   QKV_ROPE       the QKV projection straight into the attention operands: the
 //                  Q and K columns are RMS-normalised per (row, head) and
 //                  rotated (3-axis RoPE) from the fp32 accumulators, written
-//                  head-major; the V columns are written transposed (V^T).
+//                  head-major (Q' times the attention's logit scale
+//                  softmax_scale * log2 e); the V columns are written
+//                  transposed (V^T).
 //                  Page "MiniMax H3 Inference Engine voor Mac computers",
 //                  checkpoint layout notes: the QK normalisation and RoPE run
 //                  fused on the projection output.
@@ -109,7 +111,8 @@ __device__ __forceinline__ void qkv_epilogue(const GemmLaunch &a, f32x16 (&acc)[
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float tot = ss[i] + red[((wave ^ 1) * 4 + i) * 32 + l32];
-            const float rn = 1.0f / sqrtf(tot * (1.0f / kHeadDim) + a.eps);
+            // Q' also carries the attention's logit scale
+            const float rn = (tensor ? 1.0f : a.qscale) / sqrtf(tot * (1.0f / kHeadDim) + a.eps);
             const int m = m0 + 128 * wm + 32 * i + l32;
             // rows past the sequence are zero: any in-range table row serves
             const float2 *rope = a.rope + (int64_t)min(m, a.M - 1) * 3 * F;

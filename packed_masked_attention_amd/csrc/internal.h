@@ -48,6 +48,7 @@ hipError_t launch_layout_build(const LayoutLaunch &a, hipStream_t s);
 struct PrepLaunch {
     int32_t L, Lp, H, F;
     float eps;
+    float qscale;           // factor on Q' (the attention operand's logit scale)
     double inv_freq[16];
     double pos_scale[3];    // per-axis scale of the positions (1 = integer positions)
     const uint16_t *q, *k, *v;
@@ -63,9 +64,7 @@ hipError_t launch_rope_table(const PrepLaunch &a, float2 *rope, hipStream_t s);
 // ----------------------------------------------------------------- flash
 struct FlashLaunch {
     int32_t L, Lp, H, nqt, nkt;
-    float scale_log2;  // softmax_scale * log2(e)
-    float scale;       // softmax_scale
-    const uint16_t *qh, *kh, *vt;
+    const uint16_t *qh, *kh, *vt;   // Q' carries the logit scale softmax_scale * log2(e)
     uint16_t *o;
     int64_t o_ld;
     float *lse;
@@ -78,7 +77,13 @@ struct FlashLaunch {
     int32_t *queue;
     int32_t split_items;   // S: the last S items of every XCD's share run in parts
     float *part;
+    // clock stamps of the persistent workgroups (NULL: none): per workgroup
+    // {shader clock, 100 MHz real-time clock} at its start and its end
+    uint64_t *stamps;
 };
+// the flash workspace's clock-stamp area: 4 x u64 per persistent workgroup
+constexpr int kFlashStampGroups = 1024;
+constexpr size_t kFlashStampBytes = (size_t)kFlashStampGroups * 4 * sizeof(uint64_t);
 void flash_tiles(int32_t *tile_m, int32_t *tile_n);
 // bytes of work-queue counters at the start of the flash workspace
 constexpr size_t kFlashQueueBytes = 256;
@@ -112,6 +117,7 @@ struct GemmLaunch {
     // and K columns from the fp32 accumulators, head-major Q', K' and V^T out
     int32_t Lp, H, F;
     float eps;
+    float qscale;               // factor on Q' (the attention operand's logit scale)
     const float *wq, *wk;       // norm weights [128]
     const float2 *rope;         // (cos, sin) [L][3F]
     uint16_t *qh, *kh, *vt;     // [H][Lp][128], [H][Lp][128], [H][128][Lp]

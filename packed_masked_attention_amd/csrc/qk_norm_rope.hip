@@ -15,6 +15,9 @@
 // scale is 1 except where the caller asks otherwise (the engine page's
 // 256x256 preview halves the spatial coordinates).
 //
+// Q' leaves multiplied by qscale (softmax_scale * log2 e): the attention
+// kernel then reads log2-unit logits straight out of its QK product.
+//
 // HBM-bound: per (row, head) it reads 3 x 256 B and writes 3 x 256 B.
 // Block = 64 rows x 4 heads.  The block's V loads (16 per thread) are issued
 // first and stay in flight through the rest.  Each 16-lane group owns one
@@ -147,7 +150,8 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(PrepLaunch a) {
             ss += dpp_f(ss, 2);
             ss += dpp_f(ss, 4);
             ss += dpp_f(ss, 8);
-            const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
+            // Q' also carries the attention's logit scale
+            const float r = (tensor ? 1.0f : a.qscale) / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
             const f32x4 w0 = *reinterpret_cast<const f32x4 *>(w + chunk * 8);
             const f32x4 w1 = *reinterpret_cast<const f32x4 *>(w + chunk * 8 + 4);
             float n[8];

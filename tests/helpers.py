@@ -16,6 +16,10 @@ MAX_ABS = 1.5e-2
 MEAN_ABS = 2e-3
 MEAN_REL = 1e-2
 
+# The stored query operand Q' is the normalised, rotated query times the
+# logit factor softmax_scale * log2(e) (default softmax_scale 1/sqrt(128)).
+Q_OPERAND_SCALE = np.log2(np.e) / np.sqrt(128.0)
+
 
 def say(*a):
     print(*a, flush=True)

@@ -65,14 +65,16 @@ def test_host_side_argument_errors(lib):
     fw = ctypes.c_size_t()
     assert lib.pma_flash_workspace_size(ctypes.byref(p), 16384, ctypes.byref(fw)) == 0
     # 256 B of work-queue counters, then 16 split items per XCD (of 56 x 64 / 8
-    # = 448) x 4 parts, each 256 rows x (128 channels + max + row sum) fp32
-    assert fw.value == 256 + 8 * 16 * 4 * 256 * 130 * 4
+    # = 448) x 4 parts, each 256 rows x (128 channels + max + row sum) fp32,
+    # then 1024 workgroups x 4 clock stamps of 8 bytes
+    stamps = 1024 * 4 * 8
+    assert fw.value == 256 + 8 * 16 * 4 * 256 * 130 * 4 + stamps
     # below 192 k-tiles (12288 keys) nothing is split: the counters alone
     assert lib.pma_flash_workspace_size(ctypes.byref(B.attn_params(2)), 100, ctypes.byref(n)) == 0
     assert n.value == 256
     assert lib.pma_flash_workspace_size(ctypes.byref(B.attn_params(2)), 12288, ctypes.byref(n)) == 0
     # 2 heads x 48 q-tiles: 12 items per XCD, all 12 split
-    assert n.value == 256 + 8 * 12 * 4 * 256 * 130 * 4
+    assert n.value == 256 + 8 * 12 * 4 * 256 * 130 * 4 + stamps
     assert lib.pma_flash_workspace_size(ctypes.byref(p), 0, ctypes.byref(n)) == 2
     assert lib.pma_attention_workspace_size(ctypes.byref(p), 16384, ctypes.byref(n)) == 0
     assert n.value == 3 * 56 * 16384 * 128 * 2 + fw.value

@@ -4,7 +4,8 @@ import pytest
 
 import oracle
 from packed_masked_attention_amd import synth
-from tests.helpers import AttentionRun, assert_close, bf16_to_np, sample_rows, say
+from tests.helpers import (Q_OPERAND_SCALE, AttentionRun, assert_close, bf16_to_np,
+                           sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -46,16 +47,18 @@ def test_qk_norm_rope_matches_oracle(case):
     lay = inp["layout"]
     wv = 1.0 if w is None else w.astype(np.float32).astype(np.float64)
     for name, dev, src in (("Q", r.qh, inp["q"]), ("K", r.kh, inp["k"])):
+        # the stored Q' carries the logit factor
+        c = Q_OPERAND_SCALE if name == "Q" else 1.0
         got = bf16_to_np(dev)                       # [H, Lp, D]
-        ref = oracle.qk_norm_rope(src, H, 128, wv, lay["pos"], F=F)   # [L, H, D]
+        ref = oracle.qk_norm_rope(src, H, 128, wv, lay["pos"], F=F) * c   # [L, H, D]
         if w is None:   # unit weights: unit-variance outputs, the absolute bound applies
-            assert_close(got[:, :L].transpose(1, 0, 2), ref, f"{name}' (tol)")
+            assert_close(got[:, :L].transpose(1, 0, 2) / c, ref / c, f"{name}' (tol)")
         # within one bf16 rounding (half an ulp, <= |x| 2^-8) of the fp64 value,
         # plus fp32 slack for cancellation in the rotation
         g = got[:, :L].transpose(1, 0, 2)
         _within_rounding(g, ref, name)
         # unrotated channels 6F..127 are the rounded RMSNorm
-        nrm = oracle.qk_norm_rope(src, H, 128, wv, np.zeros((L, 3), np.int32), F=F)
+        nrm = oracle.qk_norm_rope(src, H, 128, wv, np.zeros((L, 3), np.int32), F=F) * c
         _within_rounding(g[..., 6 * F:], nrm[..., 6 * F:], name + " passthrough")
         assert np.all(got[:, L:] == 0)
     vt = bf16_to_np(r.vt)                           # [H, D, Lp]
@@ -385,8 +388,9 @@ def test_qk_norm_rope_large_positions():
     lay = inp["layout"]
     wv = w.astype(np.float32).astype(np.float64)
     for name, dev, src in (("Q", r.qh, inp["q"]), ("K", r.kh, inp["k"])):
+        c = Q_OPERAND_SCALE if name == "Q" else 1.0
         got = bf16_to_np(dev)[:, :r.L].transpose(1, 0, 2)
-        ref = oracle.qk_norm_rope(src, r.H, 128, wv, lay["pos"])
+        ref = oracle.qk_norm_rope(src, r.H, 128, wv, lay["pos"]) * c
         _within_rounding(got, ref, name + " large positions")
 
 

@@ -18,7 +18,7 @@ import pytest
 import oracle
 from oracle import block as oblock
 from packed_masked_attention_amd import synth
-from tests.helpers import bf16_to_np, one_rounding, say, to_dev_bf16
+from tests.helpers import Q_OPERAND_SCALE, bf16_to_np, one_rounding, say, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -216,8 +216,9 @@ def test_qkv_projection_matches_oracle(F, L, H, hidden, sc, pmax):
     A64, W64 = oracle.bf16_to_f64(a_bits), oracle.bf16_to_f64(w_bits)
     q, k, v = (A64 @ W64[i * HD:(i + 1) * HD].T for i in range(3))
     for name, got_t, x, wv in (("q'", qh, q, wq), ("k'", kh, k, wk)):
+        c = Q_OPERAND_SCALE if name == "q'" else 1.0   # the stored Q' carries the logit factor
         ref = oracle.qk_norm_rope(x, H, 128, wv.astype(np.float64), pos, F=F,
-                                  pos_scale=sc).transpose(1, 0, 2)
+                                  pos_scale=sc).transpose(1, 0, 2) * c
         got = bf16_to_np(got_t)
         err = np.abs(got[:, :L] - ref)
         bad = err > _one_rounding(ref)
