@@ -175,8 +175,9 @@ __device__ __forceinline__ float half_sum(float x) {
 // first the items of their own XCD's share (local indices [0, per_xcd - S),
 // in order, so its heads' K/V stay in its L2), then the remaining items of
 // the other XCDs' shares (neighbours first), then the kSplitParts parts of
-// the last S items of every share.  An XCD that runs ahead takes over the
-// tail of a slower one's share.
+// the last S items of every share: its own XCD's parts first (their heads'
+// K/V sit in its L2), then the others' (neighbours first).  An XCD that runs
+// ahead takes over the tail of a slower one's share.
 __device__ __forceinline__ int2 next_work(const FlashLaunch &a, int xcd, int iter) {
     const int total = a.H * a.nqt;
     const int per_xcd = (total + 7) / 8;
@@ -194,13 +195,20 @@ __device__ __forceinline__ int2 next_work(const FlashLaunch &a, int xcd, int ite
         const int w = atomicAdd(&a.queue[y], 1);
         if (w < own) return make_int2(y * per_xcd + w, -1);
     }
-    for (;;) {
-        const int g = atomicAdd(&a.queue[8], 1);
-        if (g >= 8 * S * kSplitParts) return make_int2(-1, -1);
-        const int x = g / (S * kSplitParts), sp = g % (S * kSplitParts);
-        const int item = x * per_xcd + per_xcd - S + sp / kSplitParts;
-        if (item < total) return make_int2(item, sp % kSplitParts);
+    // parts: this XCD's own first (its heads' K/V are in its L2), then the
+    // other XCDs' (neighbours first)
+    for (int k = 0; k < 8; ++k) {
+        const int y = (xcd + k) & 7;
+        if (__hip_atomic_load(&a.queue[8 + y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= S * kSplitParts)
+            continue;
+        for (;;) {
+            const int g = atomicAdd(&a.queue[8 + y], 1);
+            if (g >= S * kSplitParts) break;
+            const int item = y * per_xcd + per_xcd - S + g / kSplitParts;
+            if (item < total) return make_int2(item, g % kSplitParts);
+        }
     }
+    return make_int2(-1, -1);
 }
 
 typedef __attribute__((address_space(4))) const FlashLaunch *kernarg_launch;

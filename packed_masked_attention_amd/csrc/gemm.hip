@@ -22,33 +22,55 @@
 //                  fused on the projection output.
 //
 // Design: 256 x 256 output tile (SWIGLU: 256 rows x 128 outputs built from
-// 128 gate rows + 128 up rows of W), K in steps of 64, eight waves (two per
-// SIMD) in a 2 x 4 grid each owning a 128 x 64 block as 4 x 2 MFMA
-// 32x32x16 tiles, so the 128 fp32 accumulators stay in VGPRs.  The MFMA
-// computes D = W A^T (weights as the A operand), so a lane's accumulator
-// column is one output ROW: per-row epilogue data (tag, timestep, residual
-// row) is lane-constant and each lane writes runs of 4 consecutive bf16.
-// Both operand tiles stream into LDS with buffer_load ... lds (rows past M
-// read as zero through the buffer bound), double-buffered, 16-byte chunks
-// XOR-swizzled by row so the fragment reads are bank-conflict-free.  Tiles
-// are ordered in groups of 8 row-tiles and dealt out XCD-aware so each XCD
-// works on a compact region sharing A and W panels in its L2.
+// 128 gate rows + 128 up rows of W), four waves (one per SIMD) in a 2 x 2
+// grid, each owning a 128 x 128 block as 4 x 4 MFMA 32x32x16 tiles: 256 fp32
+// accumulators per lane, which live in the accumulation registers, and per
+// 16-deep k-step 16 independent MFMAs on 8 fragment reads (0.5 KB of LDS per
+// MFMA).  The MFMA computes D = W A^T (weights as the A operand), so a lane's
+// accumulator column is one output ROW: per-row epilogue data (tag, timestep,
+// residual row) is lane-constant and each lane writes runs of 4 consecutive
+// bf16.  Both operand tiles stream into LDS with buffer_load ... lds (rows
+// past M read as zero through the buffer bound) through a 5-deep ring of
+// 32-deep K stages (160 KB): each stage's DMA is issued four stages ahead and
+// has three stages of MFMAs to land, the waits at stage ends leave the two
+// newest stages in flight, and each wave reads its next k-step's fragments a
+// k-step ahead, across stage ends.  16-byte chunks are XOR-swizzled by row so
+// the fragment reads are bank-conflict-free.  Tiles are ordered in groups of
+// 8 row-tiles and dealt out XCD-aware so each XCD works on a compact region
+// sharing A and W panels in its L2.
 #include "internal.h"
 
 namespace pma {
 namespace {
 
+constexpr int kNW = 4;         // waves per workgroup, one per SIMD
 constexpr int kTM = 256;       // rows of A per tile
 constexpr int kTN = 256;       // rows of W per tile
-constexpr int kTK = 64;        // K per stage
-constexpr int kTileElems = kTM * kTK;   // 16384 bf16 = 32 KB per operand tile
+constexpr int kTK = 32;        // K per stage
+constexpr int kStageElems = kTM * kTK;  // 8192 bf16 = 16 KB per operand per stage
+constexpr int kDmaPerStage = 8;         // 1 KB DMA instructions per wave per stage (4 A, 4 W)
 constexpr int kGroupM = 8;
+static_assert(kTM == kTN && kTM * kTK * 2 == 16 * 1024, "16 wave-instructions of 1 KB per operand stage");
+static_assert(kDmaPerStage * kNW == 32, "each wave issues its share of a stage's 32 instructions");
+
+// End of a stage: this wave's DMA instructions, all but the newest n, have
+// landed; then the workgroup barrier (a plain s_barrier: the release fence of
+// __syncthreads() would wait for every DMA in flight, and fragment reads of
+// the next stage may stay in flight across it)
+#define PMA_STAGE_END(n)                                                                    \
+    do {                                                                                     \
+        __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14)); \
+        asm volatile("s_barrier" ::: "memory");                                             \
+    } while (0)
 constexpr int kRsrcFlags = 0x00020000;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// LDS position of 16-byte chunk c (0..7) of tile row r (128-byte rows).
-__device__ __forceinline__ int g_pos(int r, int c) { return c ^ ((r >> 1) & 7); }
+// LDS position of 16-byte chunk c (0..3) of tile row r (64-byte rows).  A
+// 16-byte fragment read is served 16 lanes (16 consecutive rows, one chunk)
+// per cycle from 256 bytes of banks; rotating the chunk by (r >> 2) & 3
+// puts those 16 rows' chunks in 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int g_pos(int r, int c) { return c ^ ((r >> 2) & 3); }
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_void *l, uint32_t voff,
                                       uint32_t soff) {
@@ -67,68 +89,56 @@ constexpr int kEpiQkvF8 = kEpiQkvRope + 1;
 
 // The QKV projection's epilogue.  The 256-column tile lies inside one of Q,
 // K, V (H even) and holds two heads; wave (wm, wn) has tokens
-// m0 + 128 wm + [0, 128) and channels 64 (wn & 1) + [0, 64) of head wn / 2.
-// A lane's registers for one token: acc[i][j][v] = channel
-// 64 (wn & 1) + 32 j + 8 (v / 4) + 4 hi + v % 4 of token m0 + 128 wm + 32 i + l32.
-// Rows past the sequence have all-zero accumulators (their A rows read as
-// zero), so the padding rows up to Lp come out as zeros.
+// m0 + 128 wm + [0, 128) and all 128 channels of head wn.  A lane's registers
+// for one token: acc[i][j][v] = channel 32 j + 8 (v / 4) + 4 hi + v % 4 of
+// token m0 + 128 wm + 32 i + l32.  Rows past the sequence have all-zero
+// accumulators (their A rows read as zero), so the padding rows up to Lp come
+// out as zeros.  st: this wave's 32 KB of LDS for the V^T staging.
 template <int F>
-__device__ __forceinline__ void qkv_epilogue(const GemmLaunch &a, f32x16 (&acc)[4][2], int m0,
-                                             int n0, int wave, int wm, int wn, int l32, int hi,
-                                             uint16_t *as0, uint16_t *as1, uint16_t *ws0,
-                                             uint16_t *ws1) {
+__device__ __forceinline__ void qkv_epilogue(const GemmLaunch &a, f32x16 (&acc)[4][4], int m0,
+                                             int n0, int wm, int wn, int l32, int hi,
+                                             uint16_t *st) {
     const int HD = a.H * kHeadDim;
     const int tensor = n0 / HD;                        // 0 Q, 1 K, 2 V
-    const int head = (n0 - tensor * HD) / kHeadDim + (wn >> 1);
-    const int cb = 64 * (wn & 1);                      // the wave's first channel in the head
+    const int head = (n0 - tensor * HD) / kHeadDim + wn;
     if (tensor < 2) {
-        // sum of squares per token: the lane's 32 channels, the other lane
-        // half's 32, then the paired wave's 64 through LDS
-        float *red = reinterpret_cast<float *>(as0);  // [8 waves][4][32]
-        float ss[4];
+        const float *w = tensor ? a.wk : a.wq;
+        uint16_t *dst = (tensor ? a.kh : a.qh) + (int64_t)head * a.Lp * kHeadDim;
+        // Q' also carries the attention's logit scale
+        const float fac = tensor ? 1.0f : a.qscale;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            // sum of squares of the token's 128 channels: the lane's 64, then
+            // the other lane half's 64
             float t = 0.f;
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) t = fmaf(acc[i][j][v], acc[i][j][v], t);
             const uint32_t u = __float_as_uint(t);
             const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-            ss[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-            if (hi == 0) red[(wave * 4 + i) * 32 + l32] = ss[i];
-        }
-        __syncthreads();
-        const float *w = tensor ? a.wk : a.wq;
-        uint16_t *dst = (tensor ? a.kh : a.qh) + (int64_t)head * a.Lp * kHeadDim;
-        // the lane's 32 norm weights: channels cb + 32 j + 8 g + 4 hi + [0, 4)
-        f32x4 wv[2][4];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                wv[j][g] = *reinterpret_cast<const f32x4 *>(w + cb + 32 * j + 8 * g + 4 * hi);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float tot = ss[i] + red[((wave ^ 1) * 4 + i) * 32 + l32];
-            // Q' also carries the attention's logit scale
-            const float rn = (tensor ? 1.0f : a.qscale) / sqrtf(tot * (1.0f / kHeadDim) + a.eps);
+            const float tot = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+            const float rn = fac / sqrtf(tot * (1.0f / kHeadDim) + a.eps);
             const int m = m0 + 128 * wm + 32 * i + l32;
             // rows past the sequence are zero: any in-range table row serves
             const float2 *rope = a.rope + (int64_t)min(m, a.M - 1) * 3 * F;
+            uint16_t *drow = dst + (int64_t)m * kHeadDim + 4 * hi;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < 4; ++j) {
                 float n[16];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) n[v] = acc[i][j][v] * rn * wv[j][v / 4][v % 4];
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 wv = *reinterpret_cast<const f32x4 *>(w + 32 * j + 8 * g + 4 * hi);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) n[4 * g + e] = acc[i][j][4 * g + e] * rn * wv[e];
+                }
                 float y[16];
-                const int c0 = cb + 32 * j;             // first channel of this 32-channel run
-                // registers v = 4 q + e hold channel c0 + 8 q + 4 hi + e; a group
+                // registers v = 4 q + e hold channel 32 j + 8 q + 4 hi + e; a group
                 // of four is wholly rotated (c < 6F, four consecutive angles of
                 // one section, partner F/2 registers away) or wholly passed on
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int c = c0 + 8 * q + 4 * hi;
+                    const int c = 32 * j + 8 * q + 4 * hi;
                     if (c < 6 * F) {
                         const int sec = c / (2 * F), f = c % F;
                         const bool first = ((q & (F >> 3)) == 0);
@@ -147,24 +157,22 @@ __device__ __forceinline__ void qkv_epilogue(const GemmLaunch &a, f32x16 (&acc)[
                         for (int e = 0; e < 4; ++e) y[4 * q + e] = n[4 * q + e];
                     }
                 }
-                uint16_t *drow = dst + (int64_t)m * kHeadDim + c0 + 4 * hi;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     uint2 o;
                     o.x = pack_bf16x2(y[4 * g], y[4 * g + 1]);
                     o.y = pack_bf16x2(y[4 * g + 2], y[4 * g + 3]);
-                    *reinterpret_cast<uint2 *>(drow + 8 * g) = o;
+                    *reinterpret_cast<uint2 *>(drow + 32 * j + 8 * g) = o;
                 }
             }
         }
     } else {
-        // V^T: each wave stages its 64 channels x 128 tokens in its own 16 KB
-        // of LDS, then writes 256-byte channel rows (tokens contiguous)
-        uint16_t *st = (wave < 2 ? as0 : wave < 4 ? as1 : wave < 6 ? ws0 : ws1) + (wave & 1) * 8192;
+        // V^T: each wave stages its 128 channels x 128 tokens in its own 32 KB
+        // of LDS (st), then writes 256-byte channel rows (tokens contiguous)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int cl = 32 * j + 8 * (v / 4) + 4 * hi + v % 4;
@@ -172,9 +180,9 @@ __device__ __forceinline__ void qkv_epilogue(const GemmLaunch &a, f32x16 (&acc)[
                 }
         // the wave reads back only what it wrote; LDS keeps a wave's accesses in order
         const int lane = l32 + 32 * hi;
-        uint16_t *vbase = a.vt + ((int64_t)head * kHeadDim + cb) * a.Lp + m0 + 128 * wm;
+        uint16_t *vbase = a.vt + (int64_t)head * kHeadDim * a.Lp + m0 + 128 * wm;
 #pragma unroll
-        for (int it = 0; it < 16; ++it) {
+        for (int it = 0; it < 32; ++it) {
             const int row = it * 4 + (lane >> 4), ch = lane & 15;
             const uint4 val = *reinterpret_cast<const uint4 *>(st + row * 128 + ch * 8);
             *reinterpret_cast<uint4 *>(vbase + (int64_t)row * a.Lp + ch * 8) = val;
@@ -183,15 +191,20 @@ __device__ __forceinline__ void qkv_epilogue(const GemmLaunch &a, f32x16 (&acc)[
 }
 
 template <int EPI>
-__global__ __launch_bounds__(512, 1) void gemm_kernel(GemmLaunch a) {
-    __shared__ __attribute__((aligned(1024))) uint16_t as0[kTileElems];
-    __shared__ __attribute__((aligned(1024))) uint16_t as1[kTileElems];
-    __shared__ __attribute__((aligned(1024))) uint16_t ws0[kTileElems];
-    __shared__ __attribute__((aligned(1024))) uint16_t ws1[kTileElems];
+__global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
+    // the ring: stage slot x holds A rows [256][32], then W rows [256][32];
+    // one object per slot, so the compiler can tell the slot being streamed
+    // into from the ones being read
+    __shared__ __attribute__((aligned(1024))) uint16_t sl0[2 * kStageElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sl1[2 * kStageElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sl2[2 * kStageElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sl3[2 * kStageElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sl4[2 * kStageElems];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hi = lane >> 5;
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave >> 1, wn = wave & 1;
 
     // ---- tile (XCD-aware, grouped)
     const int tiles_m = (a.M + kTM - 1) / kTM;
@@ -214,12 +227,14 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmLaunch a) {
     const uint32_t a_bytes = (uint32_t)(a.M - m0) * (uint32_t)a.lda * 2u;
     const __amdgpu_buffer_rsrc_t ars = make_rsrc(a.A + (int64_t)m0 * a.lda, a_bytes);
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(a.W, a.w_bytes);
-    // wave-instruction j (0..31) fills tile rows 8j..8j+7; this wave issues j = 4*wave + i
+    // wave-instruction j (0..15) of an operand stage fills tile rows 16j..16j+15
+    // (lane l: row 16j + l/4, position l%4, fetching the chunk the swizzle
+    // places there); this wave issues j = 4*wave + i of both operands
     uint32_t avo[4], wvo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int j = 4 * wave + i;
-        const int r = 8 * j + (lane >> 3), p = lane & 7, c = g_pos(r, p);
+        const int r = 16 * j + (lane >> 2), p = lane & 3, c = g_pos(r, p);
         avo[i] = 2u * ((uint32_t)r * (uint32_t)a.lda + 8u * c);
         int wrow;
         if (EPI == PMA_EPI_SWIGLU) {
@@ -231,86 +246,118 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmLaunch a) {
         }
         wvo[i] = 2u * ((uint32_t)wrow * (uint32_t)a.ldw + 8u * c);
     }
-    auto dma = [&](int k0, uint16_t *ad, uint16_t *wd) __attribute__((always_inline)) {
-        const uint32_t so = 2u * (uint32_t)k0;
+    // wave-instruction i of this wave's share of stage st's A (i < 4) or W
+    // (i >= 4) rows, into slot sl.  Stages past the last re-read the last one
+    // (into a slot no wave reads again), so every stage issues the same
+    // number of DMA instructions and the waits need no branches.
+    const int nk = a.K / kTK;   // >= 2, even
+    auto dma1 = [&](int st, uint16_t *sl, int i) __attribute__((always_inline)) {
+        const uint32_t so = 2u * (uint32_t)(min(st, nk - 1) * kTK);
+        if (i < 4)
+            dma16(ars, (lds_void *)&sl[(4 * wave + i) * 512], avo[i], so);
+        else
+            dma16(wrs, (lds_void *)&sl[kStageElems + (4 * wave + i - 4) * 512], wvo[i - 4], so);
+    };
+    auto dma = [&](int st, uint16_t *sl) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int j = 4 * wave + i;
-            dma16(ars, (lds_void *)&ad[j * 512], avo[i], so);
-            dma16(wrs, (lds_void *)&wd[j * 512], wvo[i], so);
-        }
+        for (int i = 0; i < kDmaPerStage; ++i) dma1(st, sl, i);
     };
 
-    f32x16 acc[4][2];
+    f32x16 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    // fragment rows of this lane in the two tiles
-    const int arow0 = 128 * wm + l32, wrow0 = 64 * wn + l32;
-    // one K-tile: four k-steps of 16; the fragments of step kk+1 are read
-    // while step kk's 16 MFMAs run
-    auto load_frags = [&](const uint16_t *at, const uint16_t *wt, int kk, bf16x8 (&af)[4],
-                          bf16x8 (&wf)[2]) __attribute__((always_inline)) {
+    // fragment rows of this lane in the two tiles; fragments of a k-step (16
+    // deep) are read one k-step ahead of their MFMAs, across stage ends too,
+    // in the order the MFMAs first use them
+    const int arow0 = 128 * wm + l32, wrow0 = 128 * wn + l32;
+    bf16x8 af[2][4], wf[2][4];
+    auto load_frags = [&](const uint16_t *at, const uint16_t *wt, int kk, bf16x8 (&fa)[4],
+                          bf16x8 (&fw)[4]) __attribute__((always_inline)) {
+        fa[0] = *reinterpret_cast<const bf16x8 *>(at + arow0 * kTK + 8 * g_pos(arow0, 2 * kk + hi));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = arow0 + 32 * i;
-            af[i] = *reinterpret_cast<const bf16x8 *>(at + r * kTK + 8 * g_pos(r, 2 * kk + hi));
+        for (int j = 0; j < 4; ++j) {
+            const int q = wrow0 + 32 * j;
+            fw[j] = *reinterpret_cast<const bf16x8 *>(wt + q * kTK + 8 * g_pos(q, 2 * kk + hi));
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int q = wrow0 + 32 * j;
-            wf[j] = *reinterpret_cast<const bf16x8 *>(wt + q * kTK + 8 * g_pos(q, 2 * kk + hi));
+        for (int i = 1; i < 4; ++i) {
+            const int r = arow0 + 32 * i;
+            fa[i] = *reinterpret_cast<const bf16x8 *>(at + r * kTK + 8 * g_pos(r, 2 * kk + hi));
         }
     };
-    auto compute = [&](const uint16_t *at, const uint16_t *wt) __attribute__((always_inline)) {
-        bf16x8 af0[4], wf0[2], af1[4], wf1[2];
-        load_frags(at, wt, 0, af0, wf0);
+    auto mfmas = [&](bf16x8 (&fa)[4], bf16x8 (&fw)[4]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            bf16x8 (&ac)[4] = (kk & 1) ? af1 : af0;
-            bf16x8 (&wc)[2] = (kk & 1) ? wf1 : wf0;
-            bf16x8 (&an)[4] = (kk & 1) ? af0 : af1;
-            bf16x8 (&wn_)[2] = (kk & 1) ? wf0 : wf1;
-            if (kk + 1 < 4) load_frags(at, wt, kk + 1, an, wn_);
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wc[j], ac[i], acc[i][j],
-                                                                        0, 0, 0);
-            if (kk + 1 < 4) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-            }
-        }
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[j], fa[i], acc[i][j], 0, 0, 0);
     };
 
-    const int nk = a.K / kTK;
-    dma(0, as0, ws0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt += 2) {
-        if (kt + 1 < nk) dma((kt + 1) * kTK, as1, ws1);
-        compute(as0, ws0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (kt + 1 < nk) {
-            if (kt + 2 < nk) dma((kt + 2) * kTK, as0, ws0);
-            compute(as1, ws1);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
+    // Stage s sits in slot s % 5.  During stage s every wave issues its share
+    // of stage s+4 (into the slot of stage s-1, which every wave finished
+    // reading before the previous barrier) and reads the first fragments of
+    // stage s+1.  At the end of stage s each wave waits until its share of
+    // stage s+2 has landed (stages s+3, s+4 may stay in flight), then the
+    // workgroup barrier makes stage s+2 readable by all: a stage has three
+    // stages of MFMAs to land, and no wave waits on a fragment read after
+    // the barrier.
+    // cur: slot of stage st; nxt: slot of stage st+1; dst: slot of st+4
+    auto stage = [&](int st, const uint16_t *cur, const uint16_t *nxt, uint16_t *dst)
+                     __attribute__((always_inline)) {
+        load_frags(cur, cur + kStageElems, 1, af[1], wf[1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma1(st + 4, dst, i);
+        mfmas(af[0], wf[0]);
+        load_frags(nxt, nxt + kStageElems, 0, af[0], wf[0]);
+#pragma unroll
+        for (int i = 4; i < 8; ++i) dma1(st + 4, dst, i);
+        mfmas(af[1], wf[1]);
+        // MFMAs with a fragment read after every other one and a DMA
+        // instruction after every fourth
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (i % 4 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
+        PMA_STAGE_END(2 * kDmaPerStage);
+    };
+
+    // ---- prologue: stages 0..3 requested, 0 and 1 landed
+    dma(0, sl0);
+    dma(1, sl1);
+    dma(2, sl2);
+    dma(3, sl3);
+    PMA_STAGE_END(2 * kDmaPerStage);
+    load_frags(sl0, sl0 + kStageElems, 0, af[0], wf[0]);
+
+    int st = 0;
+    for (; st + 5 <= nk; st += 5) {
+        stage(st, sl0, sl1, sl4);
+        stage(st + 1, sl1, sl2, sl0);
+        stage(st + 2, sl2, sl3, sl1);
+        stage(st + 3, sl3, sl4, sl2);
+        stage(st + 4, sl4, sl0, sl3);
     }
+    // st % 5 == 0 here
+    if (st < nk) stage(st, sl0, sl1, sl4), ++st;
+    if (st < nk) stage(st, sl1, sl2, sl0), ++st;
+    if (st < nk) stage(st, sl2, sl3, sl1), ++st;
+    if (st < nk) stage(st, sl3, sl4, sl2), ++st;
+    // no DMA may still be writing when the ring is reused or released
+    PMA_STAGE_END(0);
 
     // ---- epilogue.  acc[i][j] register v: output row m0 + 128*wm + 32*i + l32,
-    // W-tile row 64*wn + 32*j + 8*(v/4) + 4*hi + v%4.
+    // W-tile row 128*wn + 32*j + 8*(v/4) + 4*hi + v%4.
     if constexpr (EPI == kEpiQkvF16 || EPI == kEpiQkvF8) {
-        qkv_epilogue<EPI == kEpiQkvF16 ? 16 : 8>(a, acc, m0, n0, wave, wm, wn, l32, hi, as0, as1,
-                                                  ws0, ws1);
+        // the ring is free again (every wave is past the last stage's barrier)
+        uint16_t *stg = wave == 0 ? sl0 : wave == 1 ? sl1 : wave == 2 ? sl2 : sl3;
+        qkv_epilogue<EPI == kEpiQkvF16 ? 16 : 8>(a, acc, m0, n0, wm, wn, l32, hi, stg);
         return;
     }
 #pragma unroll
@@ -319,15 +366,17 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmLaunch a) {
         if (m >= a.M) continue;
         uint16_t *crow = a.C + (int64_t)m * a.ldc;
         if (EPI == PMA_EPI_SWIGLU) {
-            // acc[i][0] holds the gate rows of outputs n0 + 32*wn + [0,32),
-            // acc[i][1] the matching up rows
+            // W-tile rows 128 wn + 64 jj + [0, 64) are the gate rows (acc[i][2 jj])
+            // and the up rows (acc[i][2 jj + 1]) of outputs n0 + 32 (2 wn + jj) + [0, 32)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int col = n0 + 32 * wn + 8 * g + 4 * hi;
+                    const int col = n0 + 32 * (2 * wn + jj) + 8 * g + 4 * hi;
                     float h[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        h[e] = silu(acc[i][0][4 * g + e]) * acc[i][1][4 * g + e];
+                        h[e] = silu(acc[i][2 * jj][4 * g + e]) * acc[i][2 * jj + 1][4 * g + e];
                     uint2 w;
                     w.x = pack_bf16x2(h[0], h[1]);
                     w.y = pack_bf16x2(h[2], h[3]);
@@ -345,10 +394,10 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmLaunch a) {
                     grow = a.table + ((int64_t)(tag * a.T + ts) * 6 + a.gate_chunk) * a.N;
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int col = n0 + 64 * wn + 32 * j + 8 * g + 4 * hi;
+                    const int col = n0 + 128 * wn + 32 * j + 8 * g + 4 * hi;
                     float y[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * g + e];
@@ -378,14 +427,13 @@ hipError_t launch_gemm(const GemmLaunch &a, hipStream_t s) {
     const int total = tiles_m * (a.N / out_tn);
     const int per_xcd = (total + 7) / 8;
     const dim3 grid(8 * per_xcd);
+    const int nt = kNW * 64;
     switch (a.epi) {
-        case PMA_EPI_STORE: gemm_kernel<PMA_EPI_STORE><<<grid, 512, 0, s>>>(a); break;
-        case PMA_EPI_GATE_RESIDUAL:
-            gemm_kernel<PMA_EPI_GATE_RESIDUAL><<<grid, 512, 0, s>>>(a);
-            break;
-        case PMA_EPI_SWIGLU: gemm_kernel<PMA_EPI_SWIGLU><<<grid, 512, 0, s>>>(a); break;
-        case kEpiQkvF16: gemm_kernel<kEpiQkvF16><<<grid, 512, 0, s>>>(a); break;
-        case kEpiQkvF8: gemm_kernel<kEpiQkvF8><<<grid, 512, 0, s>>>(a); break;
+        case PMA_EPI_STORE: gemm_kernel<PMA_EPI_STORE><<<grid, nt, 0, s>>>(a); break;
+        case PMA_EPI_GATE_RESIDUAL: gemm_kernel<PMA_EPI_GATE_RESIDUAL><<<grid, nt, 0, s>>>(a); break;
+        case PMA_EPI_SWIGLU: gemm_kernel<PMA_EPI_SWIGLU><<<grid, nt, 0, s>>>(a); break;
+        case kEpiQkvF16: gemm_kernel<kEpiQkvF16><<<grid, nt, 0, s>>>(a); break;
+        case kEpiQkvF8: gemm_kernel<kEpiQkvF8><<<grid, nt, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
