@@ -30,14 +30,14 @@
 // accumulator column is one output ROW: per-row epilogue data (tag, timestep,
 // residual row) is lane-constant and each lane writes runs of 4 consecutive
 // bf16.  Both operand tiles stream into LDS with buffer_load ... lds (rows
-// past M read as zero through the buffer bound) through a 5-deep ring of
-// 32-deep K stages (160 KB): each stage's DMA is issued four stages ahead and
-// has three stages of MFMAs to land, the waits at stage ends leave the two
-// newest stages in flight, and each wave reads its next k-step's fragments a
-// k-step ahead, across stage ends.  16-byte chunks are XOR-swizzled by row so
-// the fragment reads are bank-conflict-free.  Tiles are ordered in groups of
-// 8 row-tiles and dealt out XCD-aware so each XCD works on a compact region
-// sharing A and W panels in its L2.
+// past M read as zero through the buffer bound), double-buffered in 64-deep
+// K stages (full 128-byte rows per DMA lane group): one barrier per stage,
+// placed before its last k-step, lets that k-step read the next stage's
+// first fragments and frees the slot for the stage after next, which then
+// has a whole stage of MFMAs to land.  16-byte chunks are XOR-swizzled by
+// row so the fragment reads are bank-conflict-free.  Tiles are ordered in
+// groups of 8 row-tiles and dealt out XCD-aware so each XCD works on a
+// compact region sharing A and W panels in its L2.
 #include "internal.h"
 
 namespace pma {
@@ -46,17 +46,16 @@ namespace {
 constexpr int kNW = 4;         // waves per workgroup, one per SIMD
 constexpr int kTM = 256;       // rows of A per tile
 constexpr int kTN = 256;       // rows of W per tile
-constexpr int kTK = 32;        // K per stage
-constexpr int kStageElems = kTM * kTK;  // 8192 bf16 = 16 KB per operand per stage
-constexpr int kDmaPerStage = 8;         // 1 KB DMA instructions per wave per stage (4 A, 4 W)
+constexpr int kTK = 64;        // K per stage
+constexpr int kStageElems = kTM * kTK;  // 16384 bf16 = 32 KB per operand per stage
+constexpr int kDmaPerStage = 16;        // 1 KB DMA instructions per wave per stage (8 A, 8 W)
 constexpr int kGroupM = 8;
-static_assert(kTM == kTN && kTM * kTK * 2 == 16 * 1024, "16 wave-instructions of 1 KB per operand stage");
-static_assert(kDmaPerStage * kNW == 32, "each wave issues its share of a stage's 32 instructions");
+static_assert(kTM == kTN && kTM * kTK * 2 == 32 * 1024, "32 wave-instructions of 1 KB per operand stage");
+static_assert(kDmaPerStage * kNW == 64, "each wave issues its share of a stage's 64 instructions");
 
-// End of a stage: this wave's DMA instructions, all but the newest n, have
-// landed; then the workgroup barrier (a plain s_barrier: the release fence of
-// __syncthreads() would wait for every DMA in flight, and fragment reads of
-// the next stage may stay in flight across it)
+// This wave's DMA instructions, all but the newest n, have landed; then the
+// workgroup barrier (a plain s_barrier: the release fence of __syncthreads()
+// would wait for every DMA in flight)
 #define PMA_STAGE_END(n)                                                                    \
     do {                                                                                     \
         __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14)); \
@@ -66,11 +65,11 @@ constexpr int kRsrcFlags = 0x00020000;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// LDS position of 16-byte chunk c (0..3) of tile row r (64-byte rows).  A
+// LDS position of 16-byte chunk c (0..7) of tile row r (128-byte rows).  A
 // 16-byte fragment read is served 16 lanes (16 consecutive rows, one chunk)
-// per cycle from 256 bytes of banks; rotating the chunk by (r >> 2) & 3
-// puts those 16 rows' chunks in 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int g_pos(int r, int c) { return c ^ ((r >> 2) & 3); }
+// per cycle from 256 bytes of banks; rotating the chunk by (r >> 1) & 7 puts
+// those 16 rows' chunks in 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int g_pos(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_void *l, uint32_t voff,
                                       uint32_t soff) {
@@ -192,14 +191,11 @@ __device__ __forceinline__ void qkv_epilogue(const GemmLaunch &a, f32x16 (&acc)[
 
 template <int EPI>
 __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
-    // the ring: stage slot x holds A rows [256][32], then W rows [256][32];
+    // the two stage slots: A rows [256][64], then W rows [256][64];
     // one object per slot, so the compiler can tell the slot being streamed
     // into from the ones being read
     __shared__ __attribute__((aligned(1024))) uint16_t sl0[2 * kStageElems];
     __shared__ __attribute__((aligned(1024))) uint16_t sl1[2 * kStageElems];
-    __shared__ __attribute__((aligned(1024))) uint16_t sl2[2 * kStageElems];
-    __shared__ __attribute__((aligned(1024))) uint16_t sl3[2 * kStageElems];
-    __shared__ __attribute__((aligned(1024))) uint16_t sl4[2 * kStageElems];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -227,14 +223,16 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
     const uint32_t a_bytes = (uint32_t)(a.M - m0) * (uint32_t)a.lda * 2u;
     const __amdgpu_buffer_rsrc_t ars = make_rsrc(a.A + (int64_t)m0 * a.lda, a_bytes);
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(a.W, a.w_bytes);
-    // wave-instruction j (0..15) of an operand stage fills tile rows 16j..16j+15
-    // (lane l: row 16j + l/4, position l%4, fetching the chunk the swizzle
-    // places there); this wave issues j = 4*wave + i of both operands
-    uint32_t avo[4], wvo[4];
+    // wave-instruction j (0..31) of an operand stage fills tile rows 8j..8j+7
+    // (lane l: row 8j + l/8, position l%8, fetching the chunk the swizzle
+    // places there); this wave issues j = 8*wave + i of both operands.
+    // Stages past the last re-read the last one (into a slot no wave reads
+    // again), so every stage issues the same DMA instructions.
+    uint32_t avo[8], wvo[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int j = 4 * wave + i;
-        const int r = 16 * j + (lane >> 2), p = lane & 3, c = g_pos(r, p);
+    for (int i = 0; i < 8; ++i) {
+        const int j = 8 * wave + i;
+        const int r = 8 * j + (lane >> 3), p = lane & 7, c = g_pos(r, p);
         avo[i] = 2u * ((uint32_t)r * (uint32_t)a.lda + 8u * c);
         int wrow;
         if (EPI == PMA_EPI_SWIGLU) {
@@ -246,17 +244,13 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
         }
         wvo[i] = 2u * ((uint32_t)wrow * (uint32_t)a.ldw + 8u * c);
     }
-    // wave-instruction i of this wave's share of stage st's A (i < 4) or W
-    // (i >= 4) rows, into slot sl.  Stages past the last re-read the last one
-    // (into a slot no wave reads again), so every stage issues the same
-    // number of DMA instructions and the waits need no branches.
-    const int nk = a.K / kTK;   // >= 2, even
+    const int nk = a.K / kTK;   // >= 1
     auto dma1 = [&](int st, uint16_t *sl, int i) __attribute__((always_inline)) {
         const uint32_t so = 2u * (uint32_t)(min(st, nk - 1) * kTK);
-        if (i < 4)
-            dma16(ars, (lds_void *)&sl[(4 * wave + i) * 512], avo[i], so);
+        if (i < 8)
+            dma16(ars, (lds_void *)&sl[(8 * wave + i) * 512], avo[i], so);
         else
-            dma16(wrs, (lds_void *)&sl[kStageElems + (4 * wave + i - 4) * 512], wvo[i - 4], so);
+            dma16(wrs, (lds_void *)&sl[kStageElems + (8 * wave + i - 8) * 512], wvo[i - 8], so);
     };
     auto dma = [&](int st, uint16_t *sl) __attribute__((always_inline)) {
 #pragma unroll
@@ -298,57 +292,50 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[j], fa[i], acc[i][j], 0, 0, 0);
     };
 
-    // Stage s sits in slot s % 5.  During stage s every wave issues its share
-    // of stage s+4 (into the slot of stage s-1, which every wave finished
-    // reading before the previous barrier) and reads the first fragments of
-    // stage s+1.  At the end of stage s each wave waits until its share of
-    // stage s+2 has landed (stages s+3, s+4 may stay in flight), then the
-    // workgroup barrier makes stage s+2 readable by all: a stage has three
-    // stages of MFMAs to land, and no wave waits on a fragment read after
-    // the barrier.
-    // cur: slot of stage st; nxt: slot of stage st+1; dst: slot of st+4
-    auto stage = [&](int st, const uint16_t *cur, const uint16_t *nxt, uint16_t *dst)
+    // Two slots.  Stage s sits in slot s % 2.  Its four k-steps read their
+    // fragments one k-step ahead.  After the MFMAs of k-step 2 every wave has
+    // its k-step 3 fragments in registers and its share of stage s+1 landed;
+    // the barrier there frees slot s % 2 for stage s+2 (issued during k-step
+    // 3, so it has a stage of MFMAs to land) and makes stage s+1 readable,
+    // so k-step 3 reads stage s+1's first fragments.
+    auto stage = [&](int st, const uint16_t *cur, const uint16_t *nxt, uint16_t *curw)
                      __attribute__((always_inline)) {
-        load_frags(cur, cur + kStageElems, 1, af[1], wf[1]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma1(st + 4, dst, i);
-        mfmas(af[0], wf[0]);
+        for (int kk = 0; kk < 3; ++kk) {
+            load_frags(cur, cur + kStageElems, kk + 1, af[(kk + 1) & 1], wf[(kk + 1) & 1]);
+            mfmas(af[kk & 1], wf[kk & 1]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (0 << 8));   // vmcnt(0) lgkmcnt(0)
+        asm volatile("s_barrier" ::: "memory");
         load_frags(nxt, nxt + kStageElems, 0, af[0], wf[0]);
 #pragma unroll
-        for (int i = 4; i < 8; ++i) dma1(st + 4, dst, i);
+        for (int i = 0; i < kDmaPerStage; ++i) dma1(st + 2, curw, i);
         mfmas(af[1], wf[1]);
-        // MFMAs with a fragment read after every other one and a DMA
-        // instruction after every fourth
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
+        for (int i = 0; i < 16; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if (i % 4 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
-        PMA_STAGE_END(2 * kDmaPerStage);
     };
 
-    // ---- prologue: stages 0..3 requested, 0 and 1 landed
+    // ---- prologue: stages 0 and 1 requested, 0 landed
     dma(0, sl0);
     dma(1, sl1);
-    dma(2, sl2);
-    dma(3, sl3);
-    PMA_STAGE_END(2 * kDmaPerStage);
+    PMA_STAGE_END(kDmaPerStage);
     load_frags(sl0, sl0 + kStageElems, 0, af[0], wf[0]);
 
     int st = 0;
-    for (; st + 5 <= nk; st += 5) {
-        stage(st, sl0, sl1, sl4);
-        stage(st + 1, sl1, sl2, sl0);
-        stage(st + 2, sl2, sl3, sl1);
-        stage(st + 3, sl3, sl4, sl2);
-        stage(st + 4, sl4, sl0, sl3);
+    for (; st + 2 <= nk; st += 2) {
+        stage(st, sl0, sl1, sl0);
+        stage(st + 1, sl1, sl0, sl1);
     }
-    // st % 5 == 0 here
-    if (st < nk) stage(st, sl0, sl1, sl4), ++st;
-    if (st < nk) stage(st, sl1, sl2, sl0), ++st;
-    if (st < nk) stage(st, sl2, sl3, sl1), ++st;
-    if (st < nk) stage(st, sl3, sl4, sl2), ++st;
+    if (st < nk) stage(st, sl0, sl1, sl0), ++st;
     // no DMA may still be writing when the ring is reused or released
     PMA_STAGE_END(0);
 
@@ -356,7 +343,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
     // W-tile row 128*wn + 32*j + 8*(v/4) + 4*hi + v%4.
     if constexpr (EPI == kEpiQkvF16 || EPI == kEpiQkvF8) {
         // the ring is free again (every wave is past the last stage's barrier)
-        uint16_t *stg = wave == 0 ? sl0 : wave == 1 ? sl1 : wave == 2 ? sl2 : sl3;
+        uint16_t *stg = (wave < 2 ? sl0 : sl1) + (wave & 1) * kStageElems;
         qkv_epilogue<EPI == kEpiQkvF16 ? 16 : 8>(a, acc, m0, n0, wm, wn, l32, hi, stg);
         return;
     }
