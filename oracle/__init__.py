@@ -26,6 +26,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# AddressSanitizer + UndefinedBehaviorSanitizer build (tests/run_sanitizers.py)
+_SAN_PATH = os.path.join(_HERE, "liboracle_san.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+             "-fno-omit-frame-pointer", "-g"]
 _lock = threading.Lock()
 _lib = None
 
@@ -36,25 +40,28 @@ _f64p = ctypes.POINTER(ctypes.c_double)
 _f32p = ctypes.POINTER(ctypes.c_float)
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so with gcc (no fast-math)."""
-    if not force and os.path.exists(_LIB_PATH) and \
-            os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
-        return _LIB_PATH
-    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (no fast-math); with
+    sanitize, into liboracle_san.so under ASan + UBSan (loaded instead when
+    ORACLE_SANITIZED=1, with gcc's ASan runtime preloaded)."""
+    out = _SAN_PATH if sanitize else _LIB_PATH
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(_SRC):
+        return out
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared",
-           "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+           "-fno-fast-math", "-ffp-contract=off", *(SAN_FLAGS if sanitize else []),
+           _SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 def lib():
     global _lib
     with _lock:
         if _lib is None:
-            build(force=False)
-            L = ctypes.CDLL(_LIB_PATH)
+            san = os.environ.get("ORACLE_SANITIZED") == "1"
+            L = ctypes.CDLL(build(force=False, sanitize=san))
             L.oracle_bf16_value.restype = ctypes.c_double
             L.oracle_bf16_value.argtypes = [ctypes.c_uint16]
             L.oracle_bf16_round.restype = ctypes.c_uint16

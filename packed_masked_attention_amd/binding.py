@@ -15,6 +15,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpma.so")
+if os.environ.get("PMA_SANITIZED") == "1":
+    # the host-sanitized build (tests/run_sanitizers.py); needs clang's ASan
+    # runtime preloaded
+    LIB_PATH = os.path.join(_HERE, "libpma_san.so")
 
 PMA_OK = 0
 STATUS_NAMES = ["PMA_OK", "PMA_ERR_NULL", "PMA_ERR_SHAPE", "PMA_ERR_ALIGN", "PMA_ERR_WORKSPACE",

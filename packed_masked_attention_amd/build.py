@@ -16,6 +16,13 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libpma.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
+# host code under AddressSanitizer + UndefinedBehaviorSanitizer (device code
+# unchanged), for the CPU tests of the host-side checks: libpma_san.so
+SAN_LIB = os.path.join(HERE, "libpma_san.so")
+SAN_BUILD_DIR = os.path.join(ROOT, "_build_san")
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+            "-Xarch_host", "-g"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-I", os.path.join(ROOT, "include"),
@@ -35,26 +42,32 @@ def sources():
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+def _compile(src: str, sanitize: bool = False) -> str:
+    obj = os.path.join(SAN_BUILD_DIR if sanitize else BUILD_DIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"]
-    extra = EXTRA.get(os.path.basename(src), [])
+    extra = EXTRA.get(os.path.basename(src), []) + (SAN_HOST if sanitize else [])
     subprocess.run([HIPCC, *COMMON, *extra, *lang, "-c", src, "-o", obj], check=True)
     return obj
 
 
-def build(jobs: int = 8) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(jobs: int = 8, sanitize: bool = False) -> str:
+    """libpma.so; with sanitize, libpma_san.so whose host code runs under
+    ASan + UBSan (the sanitizer runtime comes from the process: the CPU test
+    run preloads clang's shared ASan runtime)."""
+    out_dir = SAN_BUILD_DIR if sanitize else BUILD_DIR
+    out = SAN_LIB if sanitize else LIB
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    subprocess.run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-Wl,--no-undefined",
-                    *objs, "-o", tmp], check=True)
-    os.replace(tmp, LIB)
-    return LIB
+        objs = list(ex.map(lambda f: _compile(f, sanitize), srcs))
+    tmp = out + ".tmp%d" % os.getpid()
+    link = [] if sanitize else ["-Wl,--no-undefined"]
+    subprocess.run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *link, *objs, "-o", tmp],
+                   check=True)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build())
+    print(build(sanitize="--sanitize" in sys.argv))
     sys.exit(0)
