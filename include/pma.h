@@ -439,7 +439,10 @@ pma_status pma_text_refiner(const pma_block_params *p, const pma_layout *text_la
  *            r in {src0[i], src1[i]}: the change the reduced blocks made to
  *            merged row i goes to both of its rows.
  * Rows are bf16 [.][hidden], hidden % 8 == 0, 16-byte aligned; x_out may
- * alias bypass.  Index entries outside [0, seq_len) are skipped. */
+ * alias bypass.  The kernels trust the plan's contents as far as memory
+ * safety goes: an entry outside [0, seq_len) is skipped (merge writes that
+ * reduced row as zeros), and a full row named twice is restored twice.
+ * pma_token_plan_check verifies a plan on the device once, before use. */
 pma_status pma_token_merge(int32_t hidden, int32_t seq_len, int32_t n_reduced,
                            const int32_t *src0, const int32_t *src1, const pma_bf16 *x,
                            pma_bf16 *xr, void *stream);
@@ -447,6 +450,20 @@ pma_status pma_token_restore(int32_t hidden, int32_t seq_len, int32_t n_reduced,
                              const int32_t *src0, const int32_t *src1, const pma_bf16 *bypass,
                              const pma_bf16 *xr_before, const pma_bf16 *xr_after,
                              pma_bf16 *x_out, void *stream);
+
+/* Check a token-reduction plan on the device: every src0 entry and every src1
+ * entry other than -1 inside [0, seq_len), and every full row named by
+ * exactly one entry.  workspace: device int32 [seq_len + 3], overwritten.
+ * Synchronises the stream and copies the verdict back: *bits (host) gets the
+ * PMA_PLAN_* bits, *first_bad_entry the first reduced row with a bad index
+ * (-1: none), *first_bad_row the first full row named by no entry or by
+ * several (-1: none).  Returns PMA_ERR_LAYOUT when any bit is set. */
+#define PMA_PLAN_BAD_INDEX     (1 << 0) /* src0 outside [0, L), or src1 outside and not -1 */
+#define PMA_PLAN_ROW_MISSING   (1 << 1) /* a full row that no entry names                 */
+#define PMA_PLAN_ROW_REPEATED  (1 << 2) /* a full row named by more than one entry        */
+pma_status pma_token_plan_check(int32_t seq_len, int32_t n_reduced, const int32_t *src0,
+                                const int32_t *src1, int32_t *workspace, void *stream,
+                                int32_t *bits, int32_t *first_bad_entry, int32_t *first_bad_row);
 
 /* ======================================================================
  * 4. Input and output path: timestep MLP, row pack, output heads

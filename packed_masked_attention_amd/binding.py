@@ -21,6 +21,7 @@ if os.environ.get("PMA_SANITIZED") == "1":
     LIB_PATH = os.path.join(_HERE, "libpma_san.so")
 
 PMA_OK = 0
+PMA_ERR_LAYOUT = 5
 STATUS_NAMES = ["PMA_OK", "PMA_ERR_NULL", "PMA_ERR_SHAPE", "PMA_ERR_ALIGN", "PMA_ERR_WORKSPACE",
                 "PMA_ERR_LAYOUT", "PMA_ERR_DEVICE", "PMA_ERR_UNSUPPORTED"]
 TILE_EMPTY, TILE_PARTIAL, TILE_FULL = 0, 1, 2
@@ -136,6 +137,8 @@ _SIGS = {
                                 ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]),
     "pma_token_merge": (_i32, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "pma_token_restore": (_i32, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "pma_token_plan_check": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, ctypes.POINTER(_i32),
+                                    ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     "pma_timestep_embed": (_i32, [ctypes.POINTER(TembParams), _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _vp]),
     "pma_pack_rows": (_i32, [ctypes.POINTER(IoParams), ctypes.POINTER(LayoutDesc), _vp, _vp, _vp,
@@ -450,6 +453,22 @@ def pma_token_restore(hidden: int, seq_len: int, src0, src1, bypass, xr_before, 
     check(lib().pma_token_restore(hidden, seq_len, src0.numel(), ptr(src0), ptr(src1),
                                   ptr(bypass), ptr(xr_before), ptr(xr_after), ptr(x_out),
                                   stream_ptr(stream)))
+
+
+def pma_token_plan_check(seq_len: int, src0, src1, workspace=None, stream=None):
+    """(bits, first_bad_entry, first_bad_row) of a token-reduction plan; bits 0 =
+    valid.  Synchronises the stream.  workspace: int32 device tensor of at least
+    seq_len + 3 entries (allocated here when None)."""
+    import torch
+    if workspace is None:
+        workspace = torch.empty(seq_len + 3, dtype=torch.int32, device=src0.device)
+    bits, fe, fr = _i32(), _i32(), _i32()
+    st = lib().pma_token_plan_check(seq_len, src0.numel(), ptr(src0), ptr(src1), ptr(workspace),
+                                    stream_ptr(stream), ctypes.byref(bits), ctypes.byref(fe),
+                                    ctypes.byref(fr))
+    if st not in (PMA_OK, PMA_ERR_LAYOUT):
+        check(st)
+    return bits.value, fe.value, fr.value
 
 
 # ------------------------------------------------------- input / output path

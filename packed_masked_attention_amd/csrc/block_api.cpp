@@ -416,6 +416,34 @@ pma_status pma_token_restore(int32_t hidden, int32_t seq_len, int32_t n_reduced,
     return PMA_OK;
 }
 
+pma_status pma_token_plan_check(int32_t seq_len, int32_t n_reduced, const int32_t *src0,
+                                const int32_t *src1, int32_t *workspace, void *stream,
+                                int32_t *bits, int32_t *first_bad_entry, int32_t *first_bad_row) {
+    if (seq_len < 1 || n_reduced < 0 || n_reduced > seq_len)
+        FAIL(PMA_ERR_SHAPE, "seq_len %d, n_reduced %d", seq_len, n_reduced);
+    if ((n_reduced && (!src0 || !src1)) || !workspace)
+        FAIL(PMA_ERR_NULL, "src0, src1 and workspace are required");
+    if (!aligned(workspace, 4)) FAIL(PMA_ERR_ALIGN, "workspace must be 4-byte aligned");
+    pma_status st;
+    if ((st = api_check_device()) != PMA_OK) return st;
+    TokenLaunch a;
+    memset(&a, 0, sizeof a);
+    a.n = n_reduced; a.L = seq_len; a.src0 = src0; a.src1 = src1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    CHECK_HIP(launch_token_plan_check(a, workspace, s), "token plan check launch");
+    int32_t h[3] = {0, 0, 0};
+    CHECK_HIP(hipMemcpyAsync(h, workspace, sizeof h, hipMemcpyDeviceToHost, s), "plan status copy");
+    CHECK_HIP(hipStreamSynchronize(s), "plan status sync");
+    const int32_t fe = h[1] == 0x7fffffff ? -1 : h[1], fr = h[2] == 0x7fffffff ? -1 : h[2];
+    if (bits) *bits = h[0];
+    if (first_bad_entry) *first_bad_entry = fe;
+    if (first_bad_row) *first_bad_row = fr;
+    if (h[0] != 0)
+        FAIL(PMA_ERR_LAYOUT, "token plan status bits 0x%x, first bad entry %d, first bad row %d", h[0],
+             fe, fr);
+    return PMA_OK;
+}
+
 // Refiner workspace: projected text [n][hidden] bf16 | stack workspace
 pma_status pma_refiner_workspace_size(const pma_block_params *p, int32_t n, int32_t T,
                                       size_t *bytes) {

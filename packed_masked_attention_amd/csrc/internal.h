@@ -208,6 +208,8 @@ struct TokenLaunch {
     uint16_t *x_out;            // restore output (may alias x)
 };
 hipError_t launch_token_merge(const TokenLaunch &a, hipStream_t s);
+// ws: int32 [3 + L] (status bits, first bad entry, first bad row, row counts)
+hipError_t launch_token_plan_check(const TokenLaunch &a, int32_t *ws, hipStream_t s);
 hipError_t launch_token_restore(const TokenLaunch &a, hipStream_t s);
 int head_max_out();
 int head_max_t();     // distinct timesteps the head kernels accept

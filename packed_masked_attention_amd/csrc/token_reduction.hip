@@ -15,6 +15,8 @@
 // 1-2 rows.
 #include "internal.h"
 
+#include <algorithm>
+
 namespace pma {
 namespace {
 
@@ -38,7 +40,13 @@ __global__ __launch_bounds__(256) void token_merge_kernel(TokenLaunch a) {
     uint16_t *dst = a.xr_out + (int64_t)i * a.hidden;
     const bool ok0 = (uint32_t)r0 < (uint32_t)a.L;
     const bool pair = (uint32_t)r1 < (uint32_t)a.L;
-    if (!ok0) return;   // the host checks; a bad entry leaves its row untouched
+    if (!ok0) {
+        // an entry outside the sequence (pma_token_plan_check reports it):
+        // the reduced row is written as zeros rather than left stale
+        for (int c = 8 * threadIdx.x; c < a.hidden; c += 8 * 256)
+            *reinterpret_cast<uint4 *>(dst + c) = make_uint4(0, 0, 0, 0);
+        return;
+    }
     const uint16_t *x0 = a.x + (int64_t)r0 * a.hidden;
     const uint16_t *x1 = a.x + (int64_t)(pair ? r1 : r0) * a.hidden;
     for (int c = 8 * threadIdx.x; c < a.hidden; c += 8 * 256) {
@@ -77,7 +85,52 @@ __global__ __launch_bounds__(256) void token_restore_kernel(TokenLaunch a) {
     }
 }
 
+// ---- plan check.  ws: [0] status bits, [1] first bad entry, [2] first full
+// row named by no entry or by several, [3 .. 3 + L) how often each full row
+// is named.  Cleared by a kernel (no memset), so the sequence can be captured.
+__global__ __launch_bounds__(256) void token_plan_clear_kernel(int32_t *ws, int32_t L) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < (int64_t)L + 3;
+         i += (int64_t)gridDim.x * 256)
+        ws[i] = (i == 1 || i == 2) ? 0x7fffffff : 0;
+}
+
+__global__ __launch_bounds__(256) void token_plan_count_kernel(TokenLaunch a, int32_t *ws) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= a.n) return;
+    const int r0 = a.src0[i], r1 = a.src1[i];
+    bool bad = false;
+    if ((uint32_t)r0 < (uint32_t)a.L)
+        atomicAdd(&ws[3 + r0], 1);
+    else
+        bad = true;
+    if ((uint32_t)r1 < (uint32_t)a.L)
+        atomicAdd(&ws[3 + r1], 1);
+    else if (r1 != -1)
+        bad = true;
+    if (bad) {
+        atomicOr(&ws[0], PMA_PLAN_BAD_INDEX);
+        atomicMin(&ws[1], i);
+    }
+}
+
+__global__ __launch_bounds__(256) void token_plan_rows_kernel(int32_t *ws, int32_t L) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= L) return;
+    const int c = ws[3 + r];
+    if (c == 1) return;
+    atomicOr(&ws[0], c == 0 ? PMA_PLAN_ROW_MISSING : PMA_PLAN_ROW_REPEATED);
+    atomicMin(&ws[2], r);
+}
+
 }  // namespace
+
+hipError_t launch_token_plan_check(const TokenLaunch &a, int32_t *ws, hipStream_t s) {
+    const int64_t words = (int64_t)a.L + 3;
+    token_plan_clear_kernel<<<(unsigned)std::min<int64_t>((words + 255) / 256, 1024), 256, 0, s>>>(ws, a.L);
+    if (a.n > 0) token_plan_count_kernel<<<(a.n + 255) / 256, 256, 0, s>>>(a, ws);
+    token_plan_rows_kernel<<<(a.L + 255) / 256, 256, 0, s>>>(ws, a.L);
+    return hipGetLastError();
+}
 
 hipError_t launch_token_merge(const TokenLaunch &a, hipStream_t s) {
     if (a.n == 0) return hipSuccess;

@@ -174,3 +174,21 @@ def test_stack_and_refiner_host_side_argument_errors(lib):
                                 fake, ctypes.c_float(1e-5), fake, fake, 1 << 40, None) == 2
     assert lib.pma_text_refiner(ctypes.byref(p), ctypes.byref(lay), 2, w, fake, fake, 5120, 5120,
                                 fake, ctypes.c_float(-1.0), fake, fake, 1 << 40, None) == 2
+
+
+def test_token_reduction_host_side_argument_errors(lib):
+    fake = ctypes.c_void_p(256)
+    out = ctypes.c_int32()
+    # merge / restore: hidden not a multiple of 8, more reduced rows than rows, NULLs
+    assert lib.pma_token_merge(60, 100, 50, fake, fake, fake, fake, None) == 2
+    assert lib.pma_token_merge(64, 100, 101, fake, fake, fake, fake, None) == 2
+    assert lib.pma_token_merge(64, 100, 50, None, fake, fake, fake, None) == 1
+    assert lib.pma_token_merge(64, 100, 50, fake, fake, ctypes.c_void_p(264), fake, None) == 3
+    assert lib.pma_token_restore(64, 100, 50, fake, fake, fake, fake, None, fake, None) == 1
+    # plan check: shape and NULL workspace before any device work
+    assert lib.pma_token_plan_check(0, 0, fake, fake, fake, None, ctypes.byref(out), None,
+                                    None) == 2
+    assert lib.pma_token_plan_check(100, 101, fake, fake, fake, None, None, None, None) == 2
+    assert lib.pma_token_plan_check(100, 50, fake, fake, None, None, None, None, None) == 1
+    assert lib.pma_token_plan_check(100, 50, fake, fake, ctypes.c_void_p(258), None, None, None,
+                                    None) == 3

@@ -112,3 +112,42 @@ def test_reduced_stack_matches_oracle():
     # the reduction changes the result (the merged rows really are merged)
     plain = oracle.bf16_to_f64(ostack.stack_forward(x_bits, temb_bits, sets, lay, dims))
     assert np.abs(plain - ref).mean() > 1e-3
+
+
+def test_token_plan_check_flags_bad_plans():
+    """pma_token_plan_check on the device: the plan builder's plans pass; a
+    src0 outside the sequence, a src1 outside it (other than -1), a row named
+    twice and a row named by no entry each set their bit and name the first
+    offending entry or row."""
+    import torch
+    from packed_masked_attention_amd import binding as B
+    lay = synth.layout_from_counts(8, (2, 3, 4), 5, 3, T=1)
+    plan = synth.token_reduction_plan(lay)
+    L = int(lay["L"])
+    src0 = torch.from_numpy(plan["src0"]).cuda()
+    src1 = torch.from_numpy(plan["src1"]).cuda()
+    say(f"token plan check: L={L}, {src0.numel()} reduced rows")
+    assert B.pma_token_plan_check(L, src0, src1) == (0, -1, -1)
+    pair = int(np.flatnonzero(plan["src1"] >= 0)[0])
+    cases = []
+    s0 = src0.clone(); s0[3] = L                       # src0 outside the sequence
+    cases.append(("src0 out of range", s0, src1, 1, 3))
+    s1 = src1.clone(); s1[pair] = -2                   # src1 neither a row nor -1
+    cases.append(("src1 out of range", src0, s1, 1, pair))
+    s1 = src1.clone(); s1[pair] = int(plan["src0"][0])  # row src0[0] named twice, src1[pair] never
+    cases.append(("row named twice", src0, s1, 2 | 4, -1))
+    for name, a, b, bits, entry in cases:
+        got = B.pma_token_plan_check(L, a, b)
+        say(f"  {name}: {got}")
+        assert got[0] & bits == bits, name
+        if bits & 1:
+            assert got[1] == entry, name
+        else:
+            assert got[1] == -1 and got[2] >= 0, name
+    # merge writes zeros for a reduced row whose src0 lies outside the sequence
+    x = torch.randn(L, 64, device="cuda").to(torch.bfloat16)
+    xr = torch.full((src0.numel(), 64), 7.0, device="cuda", dtype=torch.bfloat16)
+    bad = src0.clone(); bad[3] = L
+    B.pma_token_merge(64, L, bad, src1, x, xr)
+    torch.cuda.synchronize()
+    assert torch.all(xr[3] == 0)
