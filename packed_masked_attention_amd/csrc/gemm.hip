@@ -30,12 +30,18 @@
 // accumulator column is one output ROW: per-row epilogue data (tag, timestep,
 // residual row) is lane-constant and each lane writes runs of 4 consecutive
 // bf16.  Both operand tiles stream into LDS with buffer_load ... lds (rows
-// past M read as zero through the buffer bound), double-buffered in 64-deep
-// K stages (full 128-byte rows per DMA lane group): one barrier per stage,
+// past M read as zero through the buffer bound) in 64-deep K stages (full
+// 128-byte rows per DMA lane group), through a ring of five 32 KB slots, one
+// operand half-stage each (the whole 160 KB of LDS): one barrier per stage,
 // placed before its last k-step, lets that k-step read the next stage's
-// first fragments and frees the slot for the stage after next, which then
-// has a whole stage of MFMAs to land.  16-byte chunks are XOR-swizzled by
-// row so the fragment reads are bank-conflict-free.  Tiles are ordered in
+// first fragments and frees the stage's two slots.  With a fifth slot the
+// next halves can be requested from that barrier on, so a stage's 16 DMA
+// instructions per wave spread over four k-steps instead of one, and each
+// half still has at least two k-steps of MFMAs to land.  The loop is
+// unrolled over the ring's period of five stages (a template parameter
+// carries the stage count mod 5, so every slot index is a compile-time
+// constant).  16-byte chunks are XOR-swizzled by row so the fragment reads
+// are bank-conflict-free.  Tiles are ordered in
 // groups of 8 row-tiles and dealt out XCD-aware so each XCD works on a
 // compact region sharing A and W panels in its L2.
 #include "internal.h"
@@ -47,11 +53,9 @@ constexpr int kNW = 4;         // waves per workgroup, one per SIMD
 constexpr int kTM = 256;       // rows of A per tile
 constexpr int kTN = 256;       // rows of W per tile
 constexpr int kTK = 64;        // K per stage
-constexpr int kStageElems = kTM * kTK;  // 16384 bf16 = 32 KB per operand per stage
-constexpr int kDmaPerStage = 16;        // 1 KB DMA instructions per wave per stage (8 A, 8 W)
+constexpr int kStageElems = kTM * kTK;  // 16384 bf16 = 32 KB per operand half-stage (one slot)
 constexpr int kGroupM = 8;
 static_assert(kTM == kTN && kTM * kTK * 2 == 32 * 1024, "32 wave-instructions of 1 KB per operand stage");
-static_assert(kDmaPerStage * kNW == 64, "each wave issues its share of a stage's 64 instructions");
 
 // This wave's DMA instructions, all but the newest n, have landed; then the
 // workgroup barrier (a plain s_barrier: the release fence of __syncthreads()
@@ -189,13 +193,30 @@ __device__ __forceinline__ void qkv_epilogue(const GemmLaunch &a, f32x16 (&acc)[
     }
 }
 
-template <int EPI>
+// The DMA schedule of the interval between the barriers of stages s-1 and s:
+// per wave 16 instructions, the W half of stage s+1 (8, first) and the A half
+// of stage s+2 (8), kSched[0] of them in k-step 3 of stage s-1 and kSched[1..3]
+// in k-steps 0..2 of stage s.  Spread evenly over the MFMAs (rather than a
+// stage's 16 in one k-step) they keep the vector memory path from stalling
+// the MFMA issue.
+constexpr int kSched[4] = {4, 4, 4, 4};
+static_assert(kSched[0] + kSched[1] + kSched[2] + kSched[3] == 16, "16 instructions per interval");
+static_assert(kSched[0] <= 8, "the W half leads the interval");
+constexpr int sched_first(int q) {   // first interval position issued in slot q
+    return q == 0 ? 0 : sched_first(q - 1) + kSched[q - 1];
+}
+
+template <int EPI, int R>
 __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
-    // the two stage slots: A rows [256][64], then W rows [256][64];
+    // five 32 KB slots, each one operand half-stage (256 rows x 64 K): half h
+    // (A of stage s is h = 2s, W of stage s is h = 2s + 1) lives in slot h % 5;
     // one object per slot, so the compiler can tell the slot being streamed
     // into from the ones being read
-    __shared__ __attribute__((aligned(1024))) uint16_t sl0[2 * kStageElems];
-    __shared__ __attribute__((aligned(1024))) uint16_t sl1[2 * kStageElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t h0[kStageElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t h1[kStageElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t h2[kStageElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t h3[kStageElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t h4[kStageElems];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -223,11 +244,11 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
     const uint32_t a_bytes = (uint32_t)(a.M - m0) * (uint32_t)a.lda * 2u;
     const __amdgpu_buffer_rsrc_t ars = make_rsrc(a.A + (int64_t)m0 * a.lda, a_bytes);
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(a.W, a.w_bytes);
-    // wave-instruction j (0..31) of an operand stage fills tile rows 8j..8j+7
-    // (lane l: row 8j + l/8, position l%8, fetching the chunk the swizzle
-    // places there); this wave issues j = 8*wave + i of both operands.
-    // Stages past the last re-read the last one (into a slot no wave reads
-    // again), so every stage issues the same DMA instructions.
+    // wave-instruction j (0..31) of a half fills tile rows 8j..8j+7 (lane l:
+    // row 8j + l/8, position l%8, fetching the chunk the swizzle places
+    // there); this wave issues j = 8*wave + i, i = 0..7, of every half.
+    // Halves past the last stage re-read the last one (into a slot no wave
+    // reads again), so every stage issues the same DMA instructions.
     uint32_t avo[8], wvo[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -244,17 +265,23 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
         }
         wvo[i] = 2u * ((uint32_t)wrow * (uint32_t)a.ldw + 8u * c);
     }
-    const int nk = a.K / kTK;   // >= 1
-    auto dma1 = [&](int st, uint16_t *sl, int i) __attribute__((always_inline)) {
-        const uint32_t so = 2u * (uint32_t)(min(st, nk - 1) * kTK);
-        if (i < 8)
-            dma16(ars, (lds_void *)&sl[(8 * wave + i) * 512], avo[i], so);
-        else
-            dma16(wrs, (lds_void *)&sl[kStageElems + (8 * wave + i - 8) * 512], wvo[i - 8], so);
+    const int nk = a.K / kTK;   // >= 1, nk % 5 == R
+
+    auto slot = [&](int s) __attribute__((always_inline)) -> uint16_t * {
+        s %= 5;
+        return s == 0 ? h0 : s == 1 ? h1 : s == 2 ? h2 : s == 3 ? h3 : h4;
     };
-    auto dma = [&](int st, uint16_t *sl) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < kDmaPerStage; ++i) dma1(st, sl, i);
+    // interval position q (0..15) of the interval that ends at stage st's
+    // barrier: W half of stage st+1 (q < 8), then A half of stage st+2.
+    // P: st % 5, known at compile time.
+    auto dma_q = [&](int st, int P, int q) __attribute__((always_inline)) {
+        if (q < 8) {
+            const uint32_t so = 2u * (uint32_t)(min(st + 1, nk - 1) * kTK);
+            dma16(wrs, (lds_void *)&slot(2 * P + 3)[(8 * wave + q) * 512], wvo[q], so);
+        } else {
+            const uint32_t so = 2u * (uint32_t)(min(st + 2, nk - 1) * kTK);
+            dma16(ars, (lds_void *)&slot(2 * P + 4)[(8 * wave + q - 8) * 512], avo[q - 8], so);
+        }
     };
 
     f32x16 acc[4][4];
@@ -284,66 +311,81 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
             fa[i] = *reinterpret_cast<const bf16x8 *>(at + r * kTK + 8 * g_pos(r, 2 * kk + hi));
         }
     };
-    auto mfmas = [&](bf16x8 (&fa)[4], bf16x8 (&fw)[4]) __attribute__((always_inline)) {
+    // 16 MFMAs, with the fragment reads of the next k-step and n DMA
+    // instructions (positions q0.. of interval st) interleaved evenly
+    auto mfmas = [&](bf16x8 (&fa)[4], bf16x8 (&fw)[4], int st, int P, int q0, int n)
+                     __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < n; ++q) dma_q(st, P, q0 + q);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[j], fa[i], acc[i][j], 0, 0, 0);
-    };
-
-    // Two slots.  Stage s sits in slot s % 2.  Its four k-steps read their
-    // fragments one k-step ahead.  After the MFMAs of k-step 2 every wave has
-    // its k-step 3 fragments in registers and its share of stage s+1 landed;
-    // the barrier there frees slot s % 2 for stage s+2 (issued during k-step
-    // 3, so it has a stage of MFMAs to land) and makes stage s+1 readable,
-    // so k-step 3 reads stage s+1's first fragments.
-    auto stage = [&](int st, const uint16_t *cur, const uint16_t *nxt, uint16_t *curw)
-                     __attribute__((always_inline)) {
-#pragma unroll
-        for (int kk = 0; kk < 3; ++kk) {
-            load_frags(cur, cur + kStageElems, kk + 1, af[(kk + 1) & 1], wf[(kk + 1) & 1]);
-            mfmas(af[kk & 1], wf[kk & 1]);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-        }
-        __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (0 << 8));   // vmcnt(0) lgkmcnt(0)
-        asm volatile("s_barrier" ::: "memory");
-        load_frags(nxt, nxt + kStageElems, 0, af[0], wf[0]);
-#pragma unroll
-        for (int i = 0; i < kDmaPerStage; ++i) dma1(st + 2, curw, i);
-        mfmas(af[1], wf[1]);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            if ((i * n) / 16 != ((i + 1) * n) / 16) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
     };
 
-    // ---- prologue: stages 0 and 1 requested, 0 landed
-    dma(0, sl0);
-    dma(1, sl1);
-    PMA_STAGE_END(kDmaPerStage);
-    load_frags(sl0, sl0 + kStageElems, 0, af[0], wf[0]);
+    // Stage st (phase P = st % 5): its halves sit in slots 2P and 2P+1 (mod 5).
+    // Its four k-steps read their fragments one k-step ahead.  After the
+    // MFMAs of k-step 2 every wave has its k-step 3 fragments in registers;
+    // the wait there leaves only the A half of stage st+2 in flight (the W
+    // half of st+1 landed), and the barrier makes stage st+1 readable (k-step
+    // 3 reads its first fragments) and frees both slots of stage st: the W
+    // half of st+2 (k-step 3 on) and the A half of st+3 (next stage) go there.
+    auto stage = [&](int st, int P) __attribute__((always_inline)) {
+        const uint16_t *ca = slot(2 * P), *cw = slot(2 * P + 1);
+#pragma unroll
+        for (int kk = 0; kk < 3; ++kk) {
+            load_frags(ca, cw, kk + 1, af[(kk + 1) & 1], wf[(kk + 1) & 1]);
+            mfmas(af[kk & 1], wf[kk & 1], st, P, sched_first(kk + 1), kSched[kk + 1]);
+        }
+        // this wave's DMA instructions, all but the interval's A half, landed
+        __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (0 << 8));   // vmcnt(8) lgkmcnt(0)
+        asm volatile("s_barrier" ::: "memory");
+        load_frags(slot(2 * P + 2), slot(2 * P + 3), 0, af[0], wf[0]);
+        mfmas(af[1], wf[1], st + 1, P + 1, 0, kSched[0]);
+    };
+
+    // ---- prologue: stages 0 and the A half of 1 requested and the leading
+    // part of the W half of 1 (what k-step 3 of a stage -1 would issue);
+    // stage 0 landed
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma16(ars, (lds_void *)&h0[(8 * wave + i) * 512], avo[i], 0u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma16(wrs, (lds_void *)&h1[(8 * wave + i) * 512], wvo[i], 0u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        dma16(ars, (lds_void *)&h2[(8 * wave + i) * 512], avo[i], 2u * (uint32_t)(min(1, nk - 1) * kTK));
+#pragma unroll
+    for (int q = 0; q < kSched[0]; ++q) dma_q(0, 0, q);
+    PMA_STAGE_END(8 + kSched[0]);
+    load_frags(h0, h1, 0, af[0], wf[0]);
 
     int st = 0;
-    for (; st + 2 <= nk; st += 2) {
-        stage(st, sl0, sl1, sl0);
-        stage(st + 1, sl1, sl0, sl1);
+    for (; st + 5 <= nk; st += 5) {
+        stage(st, 0);
+        stage(st + 1, 1);
+        stage(st + 2, 2);
+        stage(st + 3, 3);
+        stage(st + 4, 4);
     }
-    if (st < nk) stage(st, sl0, sl1, sl0), ++st;
-    // no DMA may still be writing when the ring is reused or released
+    if constexpr (R > 0) stage(st, 0);
+    if constexpr (R > 1) stage(st + 1, 1);
+    if constexpr (R > 2) stage(st + 2, 2);
+    if constexpr (R > 3) stage(st + 3, 3);
+    // no DMA may still be writing when the slots are reused or released
     PMA_STAGE_END(0);
 
     // ---- epilogue.  acc[i][j] register v: output row m0 + 128*wm + 32*i + l32,
     // W-tile row 128*wn + 32*j + 8*(v/4) + 4*hi + v%4.
     if constexpr (EPI == kEpiQkvF16 || EPI == kEpiQkvF8) {
         // the ring is free again (every wave is past the last stage's barrier)
-        uint16_t *stg = (wave < 2 ? sl0 : sl1) + (wave & 1) * kStageElems;
+        uint16_t *stg = wave == 0 ? h0 : wave == 1 ? h1 : wave == 2 ? h2 : h3;
         qkv_epilogue<EPI == kEpiQkvF16 ? 16 : 8>(a, acc, m0, n0, wm, wn, l32, hi, stg);
         return;
     }
@@ -406,6 +448,17 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
     }
 }
 
+template <int EPI>
+void launch_r(const GemmLaunch &a, dim3 grid, int nt, hipStream_t s) {
+    switch ((a.K / kTK) % 5) {
+        case 0: gemm_kernel<EPI, 0><<<grid, nt, 0, s>>>(a); break;
+        case 1: gemm_kernel<EPI, 1><<<grid, nt, 0, s>>>(a); break;
+        case 2: gemm_kernel<EPI, 2><<<grid, nt, 0, s>>>(a); break;
+        case 3: gemm_kernel<EPI, 3><<<grid, nt, 0, s>>>(a); break;
+        default: gemm_kernel<EPI, 4><<<grid, nt, 0, s>>>(a); break;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmLaunch &a, hipStream_t s) {
@@ -416,11 +469,11 @@ hipError_t launch_gemm(const GemmLaunch &a, hipStream_t s) {
     const dim3 grid(8 * per_xcd);
     const int nt = kNW * 64;
     switch (a.epi) {
-        case PMA_EPI_STORE: gemm_kernel<PMA_EPI_STORE><<<grid, nt, 0, s>>>(a); break;
-        case PMA_EPI_GATE_RESIDUAL: gemm_kernel<PMA_EPI_GATE_RESIDUAL><<<grid, nt, 0, s>>>(a); break;
-        case PMA_EPI_SWIGLU: gemm_kernel<PMA_EPI_SWIGLU><<<grid, nt, 0, s>>>(a); break;
-        case kEpiQkvF16: gemm_kernel<kEpiQkvF16><<<grid, nt, 0, s>>>(a); break;
-        case kEpiQkvF8: gemm_kernel<kEpiQkvF8><<<grid, nt, 0, s>>>(a); break;
+        case PMA_EPI_STORE: launch_r<PMA_EPI_STORE>(a, grid, nt, s); break;
+        case PMA_EPI_GATE_RESIDUAL: launch_r<PMA_EPI_GATE_RESIDUAL>(a, grid, nt, s); break;
+        case PMA_EPI_SWIGLU: launch_r<PMA_EPI_SWIGLU>(a, grid, nt, s); break;
+        case kEpiQkvF16: launch_r<kEpiQkvF16>(a, grid, nt, s); break;
+        case kEpiQkvF8: launch_r<kEpiQkvF8>(a, grid, nt, s); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
