@@ -46,16 +46,17 @@
 // compact region sharing A and W panels in its L2.
 #include "internal.h"
 
+#include <atomic>
+
 namespace pma {
 namespace {
 
 constexpr int kNW = 4;         // waves per workgroup, one per SIMD
 constexpr int kTM = 256;       // rows of A per tile
-constexpr int kTN = 256;       // rows of W per tile
 constexpr int kTK = 64;        // K per stage
 constexpr int kStageElems = kTM * kTK;  // 16384 bf16 = 32 KB per operand half-stage (one slot)
 constexpr int kGroupM = 8;
-static_assert(kTM == kTN && kTM * kTK * 2 == 32 * 1024, "32 wave-instructions of 1 KB per operand stage");
+static_assert(kTM * kTK * 2 == 32 * 1024, "32 wave-instructions of 1 KB per A half-stage");
 
 // This wave's DMA instructions, all but the newest n, have landed; then the
 // workgroup barrier (a plain s_barrier: the release fence of __syncthreads()
@@ -193,21 +194,38 @@ __device__ __forceinline__ void qkv_epilogue(const GemmLaunch &a, f32x16 (&acc)[
     }
 }
 
-// The DMA schedule of the interval between the barriers of stages s-1 and s:
-// per wave 16 instructions, the W half of stage s+1 (8, first) and the A half
-// of stage s+2 (8), kSched[0] of them in k-step 3 of stage s-1 and kSched[1..3]
-// in k-steps 0..2 of stage s.  Spread evenly over the MFMAs (rather than a
-// stage's 16 in one k-step) they keep the vector memory path from stalling
-// the MFMA issue.
-constexpr int kSched[4] = {4, 4, 4, 4};
-static_assert(kSched[0] + kSched[1] + kSched[2] + kSched[3] == 16, "16 instructions per interval");
-static_assert(kSched[0] <= 8, "the W half leads the interval");
-constexpr int sched_first(int q) {   // first interval position issued in slot q
-    return q == 0 ? 0 : sched_first(q - 1) + kSched[q - 1];
-}
+// Tile shapes: 256 rows of A times TN rows of W.  TN = 256: four waves in a
+// 2 x 2 grid, 4 x 4 MFMA tiles each; TN = 224 (only the STORE and
+// GATE_RESIDUAL epilogues): four waves stacked along M, 2 x 7 MFMA tiles each
+// (64 rows x all 224 W rows), for N where 224-wide tiles fill the CUs'
+// last round of tiles better (N = 5376: 768 tiles, three full rounds on 256
+// CUs, against 672 = 2.625 rounds of 256-wide tiles).
+template <int TN> struct Tile;
+template <> struct Tile<256> { static constexpr int WM = 2, FI = 4, FJ = 4; };
+template <> struct Tile<224> { static constexpr int WM = 4, FI = 2, FJ = 7; };
 
-template <int EPI, int R>
+// The DMA schedule of the interval between the barriers of stages s-1 and s:
+// per wave the W half of stage s+1 (TN/32 instructions, first) and the A half
+// of stage s+2 (8), four in k-step 3 of stage s-1 and the rest spread over
+// k-steps 0..2 of stage s, each k-step's share evenly over its MFMAs (rather
+// than a stage's 16 in one k-step: that fills the vector memory path and the
+// MFMA issue stalls behind it).
+template <int TN> struct Sched {
+    static constexpr int NW = TN / 32;            // W instructions per wave per half
+    static constexpr int NQ = NW + 8;             // interval positions
+    static constexpr int n[4] = {4, 4, 4, NQ - 12};   // k-step 3 (previous stage), 0, 1, 2
+    static constexpr int first(int q) { return q == 0 ? 0 : first(q - 1) + n[q - 1]; }
+    static_assert(NQ - 12 >= 1 && n[0] <= NW, "the W half leads the interval");
+};
+
+template <int EPI, int R, int TN>
 __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
+    using T = Tile<TN>;
+    using S = Sched<TN>;
+    constexpr int FI = T::FI, FJ = T::FJ, NW = S::NW;
+    constexpr int WN = kNW / T::WM;
+    static_assert(TN == 256 || (EPI == PMA_EPI_STORE || EPI == PMA_EPI_GATE_RESIDUAL),
+                  "the SwiGLU and QKV epilogues need 256-wide tiles");
     // five 32 KB slots, each one operand half-stage (256 rows x 64 K): half h
     // (A of stage s is h = 2s, W of stage s is h = 2s + 1) lives in slot h % 5;
     // one object per slot, so the compiler can tell the slot being streamed
@@ -221,11 +239,11 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hi = lane >> 5;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
 
     // ---- tile (XCD-aware, grouped)
     const int tiles_m = (a.M + kTM - 1) / kTM;
-    const int out_tn = (EPI == PMA_EPI_SWIGLU) ? kTN / 2 : kTN;
+    const int out_tn = (EPI == PMA_EPI_SWIGLU) ? TN / 2 : TN;
     const int tiles_n = a.N / out_tn;
     const int total = tiles_m * tiles_n;
     const int per_xcd = (total + 7) / 8;
@@ -244,17 +262,20 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
     const uint32_t a_bytes = (uint32_t)(a.M - m0) * (uint32_t)a.lda * 2u;
     const __amdgpu_buffer_rsrc_t ars = make_rsrc(a.A + (int64_t)m0 * a.lda, a_bytes);
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(a.W, a.w_bytes);
-    // wave-instruction j (0..31) of a half fills tile rows 8j..8j+7 (lane l:
-    // row 8j + l/8, position l%8, fetching the chunk the swizzle places
-    // there); this wave issues j = 8*wave + i, i = 0..7, of every half.
-    // Halves past the last stage re-read the last one (into a slot no wave
-    // reads again), so every stage issues the same DMA instructions.
-    uint32_t avo[8], wvo[8];
+    // wave-instruction j of a half fills tile rows 8j..8j+7 (lane l: row
+    // 8j + l/8, position l%8, fetching the chunk the swizzle places there);
+    // this wave issues j = 8*wave + i (A) and j = NW*wave + i (W) of every
+    // half.  Halves past the last stage re-read the last one (into a slot no
+    // wave reads again), so every stage issues the same DMA instructions.
+    uint32_t avo[8], wvo[NW];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int j = 8 * wave + i;
-        const int r = 8 * j + (lane >> 3), p = lane & 7, c = g_pos(r, p);
+        const int r = 8 * (8 * wave + i) + (lane >> 3), c = g_pos(r, lane & 7);
         avo[i] = 2u * ((uint32_t)r * (uint32_t)a.lda + 8u * c);
+    }
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int r = 8 * (NW * wave + i) + (lane >> 3), c = g_pos(r, lane & 7);
         int wrow;
         if (EPI == PMA_EPI_SWIGLU) {
             // W-tile rows 64w..64w+63 = [gate 32w..32w+31 | up 32w..32w+31]
@@ -271,62 +292,65 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
         s %= 5;
         return s == 0 ? h0 : s == 1 ? h1 : s == 2 ? h2 : s == 3 ? h3 : h4;
     };
-    // interval position q (0..15) of the interval that ends at stage st's
-    // barrier: W half of stage st+1 (q < 8), then A half of stage st+2.
-    // P: st % 5, known at compile time.
+    // interval position q of the interval that ends at stage st's barrier: W
+    // half of stage st+1 (q < NW), then A half of stage st+2.  P: st % 5,
+    // known at compile time.
     auto dma_q = [&](int st, int P, int q) __attribute__((always_inline)) {
-        if (q < 8) {
+        if (q < NW) {
             const uint32_t so = 2u * (uint32_t)(min(st + 1, nk - 1) * kTK);
-            dma16(wrs, (lds_void *)&slot(2 * P + 3)[(8 * wave + q) * 512], wvo[q], so);
+            dma16(wrs, (lds_void *)&slot(2 * P + 3)[(NW * wave + q) * 512], wvo[q], so);
         } else {
             const uint32_t so = 2u * (uint32_t)(min(st + 2, nk - 1) * kTK);
-            dma16(ars, (lds_void *)&slot(2 * P + 4)[(8 * wave + q - 8) * 512], avo[q - 8], so);
+            dma16(ars, (lds_void *)&slot(2 * P + 4)[(8 * wave + q - NW) * 512], avo[q - NW], so);
         }
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[FI][FJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < FJ; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     // fragment rows of this lane in the two tiles; fragments of a k-step (16
     // deep) are read one k-step ahead of their MFMAs, across stage ends too,
     // in the order the MFMAs first use them
-    const int arow0 = 128 * wm + l32, wrow0 = 128 * wn + l32;
-    bf16x8 af[2][4], wf[2][4];
-    auto load_frags = [&](const uint16_t *at, const uint16_t *wt, int kk, bf16x8 (&fa)[4],
-                          bf16x8 (&fw)[4]) __attribute__((always_inline)) {
+    const int arow0 = (kTM / T::WM) * wm + l32, wrow0 = (TN / WN) * wn + l32;
+    bf16x8 af[2][FI], wf[2][FJ];
+    auto load_frags = [&](const uint16_t *at, const uint16_t *wt, int kk, bf16x8 (&fa)[FI],
+                          bf16x8 (&fw)[FJ]) __attribute__((always_inline)) {
         fa[0] = *reinterpret_cast<const bf16x8 *>(at + arow0 * kTK + 8 * g_pos(arow0, 2 * kk + hi));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < FJ; ++j) {
             const int q = wrow0 + 32 * j;
             fw[j] = *reinterpret_cast<const bf16x8 *>(wt + q * kTK + 8 * g_pos(q, 2 * kk + hi));
         }
 #pragma unroll
-        for (int i = 1; i < 4; ++i) {
+        for (int i = 1; i < FI; ++i) {
             const int r = arow0 + 32 * i;
             fa[i] = *reinterpret_cast<const bf16x8 *>(at + r * kTK + 8 * g_pos(r, 2 * kk + hi));
         }
     };
-    // 16 MFMAs, with the fragment reads of the next k-step and n DMA
+    // FI*FJ MFMAs, with the FI+FJ fragment reads of the next k-step and n DMA
     // instructions (positions q0.. of interval st) interleaved evenly
-    auto mfmas = [&](bf16x8 (&fa)[4], bf16x8 (&fw)[4], int st, int P, int q0, int n)
+    auto mfmas = [&](bf16x8 (&fa)[FI], bf16x8 (&fw)[FJ], int st, int P, int q0, int n)
                      __attribute__((always_inline)) {
+        constexpr int nM = FI * FJ, nR = FI + FJ;
+        static_assert(nR <= nM, "at most one fragment read after each MFMA");
 #pragma unroll
         for (int q = 0; q < n; ++q) dma_q(st, P, q0 + q);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < FI; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < FJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[j], fa[i], acc[i][j], 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < nM; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if ((i * n) / 16 != ((i + 1) * n) / 16) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            if (((i + 1) * nR + nM - 1) / nM != (i * nR + nM - 1) / nM)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if ((i * n) / nM != ((i + 1) * n) / nM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
     };
 
@@ -342,13 +366,13 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
 #pragma unroll
         for (int kk = 0; kk < 3; ++kk) {
             load_frags(ca, cw, kk + 1, af[(kk + 1) & 1], wf[(kk + 1) & 1]);
-            mfmas(af[kk & 1], wf[kk & 1], st, P, sched_first(kk + 1), kSched[kk + 1]);
+            mfmas(af[kk & 1], wf[kk & 1], st, P, S::first(kk + 1), S::n[kk + 1]);
         }
         // this wave's DMA instructions, all but the interval's A half, landed
         __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (0 << 8));   // vmcnt(8) lgkmcnt(0)
         asm volatile("s_barrier" ::: "memory");
         load_frags(slot(2 * P + 2), slot(2 * P + 3), 0, af[0], wf[0]);
-        mfmas(af[1], wf[1], st + 1, P + 1, 0, kSched[0]);
+        mfmas(af[1], wf[1], st + 1, P + 1, 0, S::n[0]);
     };
 
     // ---- prologue: stages 0 and the A half of 1 requested and the leading
@@ -357,13 +381,13 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) dma16(ars, (lds_void *)&h0[(8 * wave + i) * 512], avo[i], 0u);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(wrs, (lds_void *)&h1[(8 * wave + i) * 512], wvo[i], 0u);
+    for (int i = 0; i < NW; ++i) dma16(wrs, (lds_void *)&h1[(NW * wave + i) * 512], wvo[i], 0u);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         dma16(ars, (lds_void *)&h2[(8 * wave + i) * 512], avo[i], 2u * (uint32_t)(min(1, nk - 1) * kTK));
 #pragma unroll
-    for (int q = 0; q < kSched[0]; ++q) dma_q(0, 0, q);
-    PMA_STAGE_END(8 + kSched[0]);
+    for (int q = 0; q < S::n[0]; ++q) dma_q(0, 0, q);
+    PMA_STAGE_END(8 + S::n[0]);
     load_frags(h0, h1, 0, af[0], wf[0]);
 
     int st = 0;
@@ -381,8 +405,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
     // no DMA may still be writing when the slots are reused or released
     PMA_STAGE_END(0);
 
-    // ---- epilogue.  acc[i][j] register v: output row m0 + 128*wm + 32*i + l32,
-    // W-tile row 128*wn + 32*j + 8*(v/4) + 4*hi + v%4.
+    // ---- epilogue.  acc[i][j] register v: output row m0 + (256/WM)*wm + 32*i + l32,
+    // W-tile row (TN/WN)*wn + 32*j + 8*(v/4) + 4*hi + v%4.
     if constexpr (EPI == kEpiQkvF16 || EPI == kEpiQkvF8) {
         // the ring is free again (every wave is past the last stage's barrier)
         uint16_t *stg = wave == 0 ? h0 : wave == 1 ? h1 : wave == 2 ? h2 : h3;
@@ -390,11 +414,11 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
         return;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = m0 + 128 * wm + 32 * i + l32;
+    for (int i = 0; i < FI; ++i) {
+        const int m = m0 + (kTM / T::WM) * wm + 32 * i + l32;
         if (m >= a.M) continue;
         uint16_t *crow = a.C + (int64_t)m * a.ldc;
-        if (EPI == PMA_EPI_SWIGLU) {
+        if constexpr (EPI == PMA_EPI_SWIGLU) {
             // W-tile rows 128 wn + 64 jj + [0, 64) are the gate rows (acc[i][2 jj])
             // and the up rows (acc[i][2 jj + 1]) of outputs n0 + 32 (2 wn + jj) + [0, 32)
 #pragma unroll
@@ -423,10 +447,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
                     grow = a.table + ((int64_t)(tag * a.T + ts) * 6 + a.gate_chunk) * a.N;
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < FJ; ++j)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int col = n0 + 128 * wn + 32 * j + 8 * g + 4 * hi;
+                    const int col = n0 + (TN / WN) * wn + 32 * j + 8 * g + 4 * hi;
                     float y[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * g + e];
@@ -448,32 +472,63 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
     }
 }
 
-template <int EPI>
+template <int EPI, int TN>
 void launch_r(const GemmLaunch &a, dim3 grid, int nt, hipStream_t s) {
     switch ((a.K / kTK) % 5) {
-        case 0: gemm_kernel<EPI, 0><<<grid, nt, 0, s>>>(a); break;
-        case 1: gemm_kernel<EPI, 1><<<grid, nt, 0, s>>>(a); break;
-        case 2: gemm_kernel<EPI, 2><<<grid, nt, 0, s>>>(a); break;
-        case 3: gemm_kernel<EPI, 3><<<grid, nt, 0, s>>>(a); break;
-        default: gemm_kernel<EPI, 4><<<grid, nt, 0, s>>>(a); break;
+        case 0: gemm_kernel<EPI, 0, TN><<<grid, nt, 0, s>>>(a); break;
+        case 1: gemm_kernel<EPI, 1, TN><<<grid, nt, 0, s>>>(a); break;
+        case 2: gemm_kernel<EPI, 2, TN><<<grid, nt, 0, s>>>(a); break;
+        case 3: gemm_kernel<EPI, 3, TN><<<grid, nt, 0, s>>>(a); break;
+        default: gemm_kernel<EPI, 4, TN><<<grid, nt, 0, s>>>(a); break;
     }
+}
+
+int device_cus() {
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 }  // namespace
 
+int gemm_tile_n(int epi, int M, int N) {
+    if ((epi != PMA_EPI_STORE && epi != PMA_EPI_GATE_RESIDUAL) || N % 224 != 0) return 256;
+    // rounds of tiles over the CUs, each round as long as its tiles are wide;
+    // the narrower tile is taken when it saves at least 5%
+    const int64_t cus = device_cus();
+    const int64_t tiles_m = (M + kTM - 1) / kTM;
+    const int64_t r256 = (tiles_m * (N / 256) + cus - 1) / cus;
+    const int64_t r224 = (tiles_m * (N / 224) + cus - 1) / cus;
+    return r224 * 224 * 100 < r256 * 256 * 95 ? 224 : 256;
+}
+
 hipError_t launch_gemm(const GemmLaunch &a, hipStream_t s) {
+    const int tn = gemm_tile_n(a.epi, a.M, a.N);
     const int tiles_m = (a.M + kTM - 1) / kTM;
-    const int out_tn = (a.epi == PMA_EPI_SWIGLU) ? kTN / 2 : kTN;
+    const int out_tn = (a.epi == PMA_EPI_SWIGLU) ? tn / 2 : tn;
     const int total = tiles_m * (a.N / out_tn);
     const int per_xcd = (total + 7) / 8;
     const dim3 grid(8 * per_xcd);
     const int nt = kNW * 64;
     switch (a.epi) {
-        case PMA_EPI_STORE: launch_r<PMA_EPI_STORE>(a, grid, nt, s); break;
-        case PMA_EPI_GATE_RESIDUAL: launch_r<PMA_EPI_GATE_RESIDUAL>(a, grid, nt, s); break;
-        case PMA_EPI_SWIGLU: launch_r<PMA_EPI_SWIGLU>(a, grid, nt, s); break;
-        case kEpiQkvF16: launch_r<kEpiQkvF16>(a, grid, nt, s); break;
-        case kEpiQkvF8: launch_r<kEpiQkvF8>(a, grid, nt, s); break;
+        case PMA_EPI_STORE:
+            if (tn == 224) launch_r<PMA_EPI_STORE, 224>(a, grid, nt, s);
+            else launch_r<PMA_EPI_STORE, 256>(a, grid, nt, s);
+            break;
+        case PMA_EPI_GATE_RESIDUAL:
+            if (tn == 224) launch_r<PMA_EPI_GATE_RESIDUAL, 224>(a, grid, nt, s);
+            else launch_r<PMA_EPI_GATE_RESIDUAL, 256>(a, grid, nt, s);
+            break;
+        case PMA_EPI_SWIGLU: launch_r<PMA_EPI_SWIGLU, 256>(a, grid, nt, s); break;
+        case kEpiQkvF16: launch_r<kEpiQkvF16, 256>(a, grid, nt, s); break;
+        case kEpiQkvF8: launch_r<kEpiQkvF8, 256>(a, grid, nt, s); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -125,6 +125,9 @@ struct GemmLaunch {
 // internal epilogue id (beside PMA_EPI_*): the fused QKV projection
 constexpr int kEpiQkvRope = 3;
 hipError_t launch_gemm(const GemmLaunch &a, hipStream_t s);
+// W rows per output tile launch_gemm takes for this problem (256, or 224
+// where that fills the last round of tiles better)
+int gemm_tile_n(int epi, int M, int N);
 
 struct LnModLaunch {
     int32_t L, hidden, T, shift_chunk;

@@ -119,11 +119,15 @@ def test_ln_modulate_matches_oracle():
 
 @pytest.mark.parametrize("epi", [0, 1, 2])
 @pytest.mark.parametrize("M", [300, 512])
-def test_linear_epilogues_match_numpy(epi, M):
+@pytest.mark.parametrize("N,K", [(512, 320), (1792, 64), (1792, 192), (1792, 256), (1792, 448)])
+def test_linear_epilogues_match_numpy(epi, M, N, K):
+    """N = 1792 with the store and gated-residual epilogues runs the 224-wide
+    tiles (one round of tiles either way, the narrower one shorter); K spans
+    every stage count mod 5 (K/64 = 5, 1, 3, 4, 7)."""
     import torch
     from packed_masked_attention_amd import binding as B
-    rng = np.random.default_rng(10 + epi)
-    N, K, T = 512, 320, 2
+    rng = np.random.default_rng(10 + epi + K)
+    T = 2
     say(f"linear epi={epi} M={M} N={N} K={K}")
     A = synth.normal_bf16(rng, (M, K))
     W = synth.normal_bf16(rng, (2 * N if epi == 2 else N, K), 0.05)
@@ -153,6 +157,52 @@ def test_linear_epilogues_match_numpy(epi, M):
     bound = np.abs(ref) * 2.0 ** -8 * 1.02 + 2e-3 * np.sqrt(np.mean(ref ** 2))
     bad = err > bound
     assert not bad.any(), f"{int(bad.sum())} values off; worst {err.max()}"
+
+
+@pytest.mark.parametrize("epi", [0, 1])
+def test_linear_tile_shapes_agree(epi):
+    """The O-projection shape (N = 5376, K = 7168) at M = 8192 runs 224-wide
+    tiles (768 tiles, three full rounds on 256 CUs, against 2.625 rounds of
+    256-wide ones) and at M = 6144 256-wide tiles (two rounds).  An output row
+    depends only on its A row and is summed over K in the same order by both
+    shapes, so the first 6144 rows agree bit for bit; a sample of rows is
+    checked against fp64."""
+    import torch
+    from packed_masked_attention_amd import binding as B
+    assert torch.cuda.get_device_properties(0).multi_processor_count == 256
+    N, K, T = 5376, 7168, 3
+    g = torch.Generator(device="cuda").manual_seed(20 + epi)
+    A = torch.randn(8192, K, device="cuda", generator=g).to(torch.bfloat16)
+    W = (torch.randn(N, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    Rr = torch.randn(8192, N, device="cuda", generator=g).to(torch.bfloat16)
+    table = torch.randn(3, T, 6, N, device="cuda", generator=g)
+    tags = torch.randint(-1, 3, (8192,), device="cuda", generator=g, dtype=torch.int32)
+    ts = torch.randint(0, T, (8192,), device="cuda", generator=g, dtype=torch.int32)
+    outs = {}
+    for M in (8192, 6144):
+        say(f"linear epi={epi} M={M} N={N} K={K}")
+        C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        B.pma_linear(M, N, K, A, K, W, K, C, N, epi, R=Rr, ldr=N, table=table, num_timesteps=T,
+                     gate_chunk=2, tags=tags, ts_idx=ts)
+        torch.cuda.synchronize()
+        outs[M] = C
+    assert torch.equal(outs[8192][:6144].view(torch.int16), outs[6144].view(torch.int16))
+    rows = np.random.default_rng(epi).choice(8192, 48, replace=False)
+    got = bf16_to_np(outs[8192][rows].contiguous())
+    a64 = bf16_to_np(A[rows].contiguous())
+    acc = a64 @ bf16_to_np(W).T
+    if epi == 0:
+        ref = acc
+    else:
+        tg, tsn = tags[rows].cpu().numpy(), ts[rows].cpu().numpy()
+        tab = table.cpu().numpy().astype(np.float64)
+        gate = np.zeros((rows.size, N))
+        real = tg >= 0
+        gate[real] = tab[tg[real], tsn[real], 2]
+        ref = bf16_to_np(Rr[rows].contiguous()) + gate * acc
+    err = np.abs(got - ref)
+    bound = np.abs(ref) * 2.0 ** -8 * 1.02 + 2e-3 * np.sqrt(np.mean(ref ** 2))
+    assert not (err > bound).any(), f"worst {err.max()}"
 
 
 _one_rounding = one_rounding
