@@ -41,9 +41,11 @@
 // unrolled over the ring's period of five stages (a template parameter
 // carries the stage count mod 5, so every slot index is a compile-time
 // constant).  16-byte chunks are XOR-swizzled by row so the fragment reads
-// are bank-conflict-free.  Tiles are ordered in
-// groups of 8 row-tiles and dealt out XCD-aware so each XCD works on a
-// compact region sharing A and W panels in its L2.
+// are bank-conflict-free.  Tiles are ordered in groups of 8 row-tiles and
+// dealt out XCD-aware so each XCD works on a compact region sharing A and W
+// panels in its L2.  A second tile shape, 256 x 224 (four waves stacked along
+// M), serves the store and gated-residual epilogues where its tile count
+// fills the CUs' last round better (see Tile below).
 #include "internal.h"
 
 #include <atomic>
