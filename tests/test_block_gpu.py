@@ -118,12 +118,13 @@ def test_ln_modulate_matches_oracle():
 
 
 @pytest.mark.parametrize("epi", [0, 1, 2])
-@pytest.mark.parametrize("M", [300, 512])
+@pytest.mark.parametrize("M", [1, 257, 300, 512])
 @pytest.mark.parametrize("N,K", [(512, 320), (1792, 64), (1792, 192), (1792, 256), (1792, 448)])
 def test_linear_epilogues_match_numpy(epi, M, N, K):
     """N = 1792 with the store and gated-residual epilogues runs the 224-wide
     tiles (one round of tiles either way, the narrower one shorter); K spans
-    every stage count mod 5 (K/64 = 5, 1, 3, 4, 7)."""
+    every stage count mod 5 (K/64 = 5, 1, 3, 4, 7); M = 1 and 257 leave a
+    tile with one real row."""
     import torch
     from packed_masked_attention_amd import binding as B
     rng = np.random.default_rng(10 + epi + K)
