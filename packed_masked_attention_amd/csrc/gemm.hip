@@ -40,7 +40,8 @@
 // half still has at least two k-steps of MFMAs to land.  The loop is
 // unrolled over the ring's period of five stages (a template parameter
 // carries the stage count mod 5, so every slot index is a compile-time
-// constant).  16-byte chunks are XOR-swizzled by row so the fragment reads
+// constant, and the remaining stages run unrolled ahead of the loop or
+// behind it).  16-byte chunks are XOR-swizzled by row so the fragment reads
 // are bank-conflict-free.  Tiles are ordered in groups of 8 row-tiles and
 // dealt out XCD-aware so each XCD works on a compact region sharing A and W
 // panels in its L2.  A second tile shape, 256 x 224 (four waves stacked along
@@ -377,22 +378,38 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
         mfmas(af[1], wf[1], st + 1, P + 1, 0, S::n[0]);
     };
 
+    // ---- the ring's phase: stage st has phase (st + P0) % 5.  With 256-wide
+    // tiles the first H stages (H = R, or a whole period when R = 0) run ahead
+    // of the unrolled loop, ending at phase 4, and the loop runs whole periods
+    // from phase 0: after a remainder placed behind the loop the compiler moved
+    // the accumulators between registers (about 3600 moves per tile, 1.5% of
+    // the kernel's time at R = 4).  The 224-wide tiles keep the remainder behind
+    // the loop, where they measured 2% faster.
+    constexpr bool kHeadPeel = TN == 256;
+    constexpr int H = !kHeadPeel ? 0 : R == 0 ? 5 : R;
+    constexpr int P0 = (5 - H) % 5;
     // ---- prologue: stages 0 and the A half of 1 requested and the leading
     // part of the W half of 1 (what k-step 3 of a stage -1 would issue);
     // stage 0 landed
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(ars, (lds_void *)&h0[(8 * wave + i) * 512], avo[i], 0u);
+    for (int i = 0; i < 8; ++i) dma16(ars, (lds_void *)&slot(2 * P0)[(8 * wave + i) * 512], avo[i], 0u);
 #pragma unroll
-    for (int i = 0; i < NW; ++i) dma16(wrs, (lds_void *)&h1[(NW * wave + i) * 512], wvo[i], 0u);
+    for (int i = 0; i < NW; ++i) dma16(wrs, (lds_void *)&slot(2 * P0 + 1)[(NW * wave + i) * 512], wvo[i], 0u);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        dma16(ars, (lds_void *)&h2[(8 * wave + i) * 512], avo[i], 2u * (uint32_t)(min(1, nk - 1) * kTK));
+        dma16(ars, (lds_void *)&slot(2 * P0 + 2)[(8 * wave + i) * 512], avo[i],
+              2u * (uint32_t)(min(1, nk - 1) * kTK));
 #pragma unroll
-    for (int q = 0; q < S::n[0]; ++q) dma_q(0, 0, q);
+    for (int q = 0; q < S::n[0]; ++q) dma_q(0, P0, q);
     PMA_STAGE_END(8 + S::n[0]);
-    load_frags(h0, h1, 0, af[0], wf[0]);
+    load_frags(slot(2 * P0), slot(2 * P0 + 1), 0, af[0], wf[0]);
 
-    int st = 0;
+    if constexpr (H > 0) stage(0, P0);
+    if constexpr (H > 1) stage(1, P0 + 1);
+    if constexpr (H > 2) stage(2, P0 + 2);
+    if constexpr (H > 3) stage(3, P0 + 3);
+    if constexpr (H > 4) stage(4, P0 + 4);
+    int st = H;
     for (; st + 5 <= nk; st += 5) {
         stage(st, 0);
         stage(st + 1, 1);
@@ -400,10 +417,12 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
         stage(st + 3, 3);
         stage(st + 4, 4);
     }
-    if constexpr (R > 0) stage(st, 0);
-    if constexpr (R > 1) stage(st + 1, 1);
-    if constexpr (R > 2) stage(st + 2, 2);
-    if constexpr (R > 3) stage(st + 3, 3);
+    if constexpr (!kHeadPeel) {
+        if constexpr (R > 0) stage(st, 0);
+        if constexpr (R > 1) stage(st + 1, 1);
+        if constexpr (R > 2) stage(st + 2, 2);
+        if constexpr (R > 3) stage(st + 3, 3);
+    }
     // no DMA may still be writing when the slots are reused or released
     PMA_STAGE_END(0);
 
