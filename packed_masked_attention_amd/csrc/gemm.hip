@@ -44,9 +44,9 @@
 // behind it).  16-byte chunks are XOR-swizzled by row so the fragment reads
 // are bank-conflict-free.  Tiles are ordered in groups of 8 row-tiles and
 // dealt out XCD-aware so each XCD works on a compact region sharing A and W
-// panels in its L2.  A second tile shape, 256 x 224 (four waves stacked along
-// M), serves the store and gated-residual epilogues where its tile count
-// fills the CUs' last round better (see Tile below).
+// panels in its L2.  Two more tile shapes fill the CUs' last round better
+// (see Tile below): 256 x 224 for the store and gated-residual epilogues, and
+// 256 x 128 for the last columns of the QKV projection, in a second launch.
 #include "internal.h"
 
 #include <atomic>
@@ -94,17 +94,20 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 constexpr int kEpiQkvF16 = kEpiQkvRope;
 constexpr int kEpiQkvF8 = kEpiQkvRope + 1;
 
-// The QKV projection's epilogue.  The 256-column tile lies inside one of Q,
-// K, V (H even) and holds two heads; wave (wm, wn) has tokens
-// m0 + 128 wm + [0, 128) and all 128 channels of head wn.  A lane's registers
-// for one token: acc[i][j][v] = channel 32 j + 8 (v / 4) + 4 hi + v % 4 of
-// token m0 + 128 wm + 32 i + l32.  Rows past the sequence have all-zero
-// accumulators (their A rows read as zero), so the padding rows up to Lp come
-// out as zeros.  st: this wave's 32 KB of LDS for the V^T staging.
-template <int F>
-__device__ __forceinline__ void qkv_epilogue(const GemmLaunch &a, f32x16 (&acc)[4][4], int m0,
+// The QKV projection's epilogue.  The tile lies inside one of Q, K, V (H
+// even): a 256-column tile holds two heads and wave (wm, wn) has tokens
+// m0 + 128 wm + [0, 128) of head wn (FI = 4); a 128-column tile holds one
+// head and wave wm has tokens m0 + 64 wm + [0, 64) (FI = 2, wn = 0).  A
+// lane's registers for one token: acc[i][j][v] = channel 32 j + 8 (v / 4) +
+// 4 hi + v % 4 of token m0 + 32 FI wm + 32 i + l32.  Rows past the sequence
+// have all-zero accumulators (their A rows read as zero), so the padding rows
+// up to Lp come out as zeros.  st: this wave's LDS (32 FI x 256 bytes) for
+// the V^T staging.
+template <int F, int FI>
+__device__ __forceinline__ void qkv_epilogue(const GemmLaunch &a, f32x16 (&acc)[FI][4], int m0,
                                              int n0, int wm, int wn, int l32, int hi,
                                              uint16_t *st) {
+    constexpr int TOK = 32 * FI;                       // tokens of a wave
     const int HD = a.H * kHeadDim;
     const int tensor = n0 / HD;                        // 0 Q, 1 K, 2 V
     const int head = (n0 - tensor * HD) / kHeadDim + wn;
@@ -114,7 +117,7 @@ __device__ __forceinline__ void qkv_epilogue(const GemmLaunch &a, f32x16 (&acc)[
         // Q' also carries the attention's logit scale
         const float fac = tensor ? 1.0f : a.qscale;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < FI; ++i) {
             // sum of squares of the token's 128 channels: the lane's 64, then
             // the other lane half's 64
             float t = 0.f;
@@ -126,7 +129,7 @@ __device__ __forceinline__ void qkv_epilogue(const GemmLaunch &a, f32x16 (&acc)[
             const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
             const float tot = __uint_as_float(r[0]) + __uint_as_float(r[1]);
             const float rn = fac / sqrtf(tot * (1.0f / kHeadDim) + a.eps);
-            const int m = m0 + 128 * wm + 32 * i + l32;
+            const int m = m0 + TOK * wm + 32 * i + l32;
             // rows past the sequence are zero: any in-range table row serves
             const float2 *rope = a.rope + (int64_t)min(m, a.M - 1) * 3 * F;
             uint16_t *drow = dst + (int64_t)m * kHeadDim + 4 * hi;
@@ -174,24 +177,25 @@ __device__ __forceinline__ void qkv_epilogue(const GemmLaunch &a, f32x16 (&acc)[
             }
         }
     } else {
-        // V^T: each wave stages its 128 channels x 128 tokens in its own 32 KB
-        // of LDS (st), then writes 256-byte channel rows (tokens contiguous)
+        // V^T: each wave stages its 128 channels x TOK tokens in its own LDS
+        // (st), then writes channel rows of TOK tokens (2 TOK contiguous bytes)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < FI; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int cl = 32 * j + 8 * (v / 4) + 4 * hi + v % 4;
-                    st[cl * 128 + 32 * i + l32] = (uint16_t)(pack_bf16x2(acc[i][j][v], 0.f) & 0xffffu);
+                    st[cl * TOK + 32 * i + l32] = (uint16_t)(pack_bf16x2(acc[i][j][v], 0.f) & 0xffffu);
                 }
         // the wave reads back only what it wrote; LDS keeps a wave's accesses in order
         const int lane = l32 + 32 * hi;
-        uint16_t *vbase = a.vt + (int64_t)head * kHeadDim * a.Lp + m0 + 128 * wm;
+        constexpr int CPR = TOK / 8;                   // 16-byte chunks per channel row
+        uint16_t *vbase = a.vt + (int64_t)head * kHeadDim * a.Lp + m0 + TOK * wm;
 #pragma unroll
-        for (int it = 0; it < 32; ++it) {
-            const int row = it * 4 + (lane >> 4), ch = lane & 15;
-            const uint4 val = *reinterpret_cast<const uint4 *>(st + row * 128 + ch * 8);
+        for (int it = 0; it < kHeadDim * CPR / 64; ++it) {
+            const int row = it * (64 / CPR) + lane / CPR, ch = lane % CPR;
+            const uint4 val = *reinterpret_cast<const uint4 *>(st + row * TOK + ch * 8);
             *reinterpret_cast<uint4 *>(vbase + (int64_t)row * a.Lp + ch * 8) = val;
         }
     }
@@ -206,6 +210,9 @@ __device__ __forceinline__ void qkv_epilogue(const GemmLaunch &a, f32x16 (&acc)[
 template <int TN> struct Tile;
 template <> struct Tile<256> { static constexpr int WM = 2, FI = 4, FJ = 4; };
 template <> struct Tile<224> { static constexpr int WM = 4, FI = 2, FJ = 7; };
+// 256 x 128 (the QKV epilogue only): four waves stacked along M, 2 x 4 MFMA
+// tiles each (64 tokens x one head), for the columns of a partial last round
+template <> struct Tile<128> { static constexpr int WM = 4, FI = 2, FJ = 4; };
 
 // The DMA schedule of the interval between the barriers of stages s-1 and s:
 // per wave the W half of stage s+1 (TN/32 instructions, first) and the A half
@@ -216,9 +223,11 @@ template <> struct Tile<224> { static constexpr int WM = 4, FI = 2, FJ = 7; };
 template <int TN> struct Sched {
     static constexpr int NW = TN / 32;            // W instructions per wave per half
     static constexpr int NQ = NW + 8;             // interval positions
-    static constexpr int n[4] = {4, 4, 4, NQ - 12};   // k-step 3 (previous stage), 0, 1, 2
+    // k-step 3 (previous stage), then k-steps 0, 1, 2 (4,4,4,4 / 4,4,4,3 / 4,3,3,2)
+    static constexpr int n[4] = {4, (NQ - 2) / 3, (NQ - 3) / 3, (NQ - 4) / 3};
     static constexpr int first(int q) { return q == 0 ? 0 : first(q - 1) + n[q - 1]; }
-    static_assert(NQ - 12 >= 1 && n[0] <= NW, "the W half leads the interval");
+    static_assert(n[0] + n[1] + n[2] + n[3] == NQ && n[3] >= 1 && n[0] <= NW,
+                  "every position once, the W half leading the interval");
 };
 
 template <int EPI, int R, int TN>
@@ -227,8 +236,9 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
     using S = Sched<TN>;
     constexpr int FI = T::FI, FJ = T::FJ, NW = S::NW;
     constexpr int WN = kNW / T::WM;
-    static_assert(TN == 256 || (EPI == PMA_EPI_STORE || EPI == PMA_EPI_GATE_RESIDUAL),
-                  "the SwiGLU and QKV epilogues need 256-wide tiles");
+    static_assert(TN == 256 || (TN == 224 && (EPI == PMA_EPI_STORE || EPI == PMA_EPI_GATE_RESIDUAL)) ||
+                      (TN == 128 && (EPI == kEpiQkvF16 || EPI == kEpiQkvF8)),
+                  "tile shapes: 224 for the store and gated residual, 128 for the QKV epilogue");
     // five 32 KB slots, each one operand half-stage (256 rows x 64 K): half h
     // (A of stage s is h = 2s, W of stage s is h = 2s + 1) lives in slot h % 5;
     // one object per slot, so the compiler can tell the slot being streamed
@@ -247,7 +257,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
     // ---- tile (XCD-aware, grouped)
     const int tiles_m = (a.M + kTM - 1) / kTM;
     const int out_tn = (EPI == PMA_EPI_SWIGLU) ? TN / 2 : TN;
-    const int tiles_n = a.N / out_tn;
+    const int tiles_n = (a.n_end - a.n_begin) / out_tn;   // output columns [n_begin, n_end)
     const int total = tiles_m * tiles_n;
     const int per_xcd = (total + 7) / 8;
     const int t = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
@@ -259,7 +269,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
     const int tm = first_m + (t % per_group) % gsize;
     const int tn = (t % per_group) / gsize;
     const int m0 = tm * kTM;
-    const int n0 = tn * out_tn;
+    const int n0 = a.n_begin + tn * out_tn;
 
     // ---- operand streams.  A rows m0.. (bound: rows < M), W rows per tile row.
     const uint32_t a_bytes = (uint32_t)(a.M - m0) * (uint32_t)a.lda * 2u;
@@ -378,14 +388,14 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
         mfmas(af[1], wf[1], st + 1, P + 1, 0, S::n[0]);
     };
 
-    // ---- the ring's phase: stage st has phase (st + P0) % 5.  With 256-wide
-    // tiles the first H stages (H = R, or a whole period when R = 0) run ahead
+    // ---- the ring's phase: stage st has phase (st + P0) % 5.  With 256- and
+    // 128-wide tiles the first H stages (H = R, or a whole period when R = 0) run ahead
     // of the unrolled loop, ending at phase 4, and the loop runs whole periods
     // from phase 0: after a remainder placed behind the loop the compiler moved
     // the accumulators between registers (about 3600 moves per tile, 1.5% of
     // the kernel's time at R = 4).  The 224-wide tiles keep the remainder behind
     // the loop, where they measured 2% faster.
-    constexpr bool kHeadPeel = TN == 256;
+    constexpr bool kHeadPeel = TN != 224;
     constexpr int H = !kHeadPeel ? 0 : R == 0 ? 5 : R;
     constexpr int P0 = (5 - H) % 5;
     // ---- prologue: stages 0 and the A half of 1 requested and the leading
@@ -431,7 +441,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
     if constexpr (EPI == kEpiQkvF16 || EPI == kEpiQkvF8) {
         // the ring is free again (every wave is past the last stage's barrier)
         uint16_t *stg = wave == 0 ? h0 : wave == 1 ? h1 : wave == 2 ? h2 : h3;
-        qkv_epilogue<EPI == kEpiQkvF16 ? 16 : 8>(a, acc, m0, n0, wm, wn, l32, hi, stg);
+        qkv_epilogue<EPI == kEpiQkvF16 ? 16 : 8, FI>(a, acc, m0, n0, wm, wn, l32, hi, stg);
         return;
     }
 #pragma unroll
@@ -530,26 +540,62 @@ int gemm_tile_n(int epi, int M, int N) {
     return r224 * 224 * 100 < r256 * 256 * 95 ? 224 : 256;
 }
 
+int gemm_qkv_narrow_columns(int M, int N) {
+    // The QKV projection's 256-wide column tiles, the last k of them run as
+    // 128-wide tiles (twice as many, each about 0.6 of a wide tile's time) in
+    // a second launch, when that shortens a problem of two or more rounds by
+    // at least 3%: at M = 8192, N = 21504 the 2688 wide tiles are 10.5 rounds
+    // on 256 CUs; 2560 wide + 256 narrow tiles are 10 rounds + one narrow one.
+    const int64_t cus = device_cus();
+    const int64_t tiles_m = (M + kTM - 1) / kTM, tn = N / 256;
+    auto est = [&](int64_t k) {
+        return 10 * ((tiles_m * (tn - k) + cus - 1) / cus) + 6 * ((2 * k * tiles_m + cus - 1) / cus);
+    };
+    const int64_t base = est(0);
+    if (base < 20) return 0;
+    int64_t best = 0, best_t = base;
+    for (int64_t k = 1; k <= tn; ++k)
+        if (est(k) < best_t) best = k, best_t = est(k);
+    return best_t * 100 <= base * 97 ? (int)(best * 256) : 0;
+}
+
+namespace {
+
+template <int EPI, int TN>
+void launch_cols(const GemmLaunch &a, int n_begin, int n_end, hipStream_t s) {
+    GemmLaunch b = a;
+    b.n_begin = n_begin;
+    b.n_end = n_end;
+    const int tiles_m = (b.M + kTM - 1) / kTM;
+    const int out_tn = (EPI == PMA_EPI_SWIGLU) ? TN / 2 : TN;
+    const int total = tiles_m * ((n_end - n_begin) / out_tn);
+    const int per_xcd = (total + 7) / 8;
+    launch_r<EPI, TN>(b, dim3(8 * per_xcd), kNW * 64, s);
+}
+
+template <int EPI>
+void launch_qkv(const GemmLaunch &a, hipStream_t s) {
+    const int narrow = gemm_qkv_narrow_columns(a.M, a.N);
+    if (narrow < a.N) launch_cols<EPI, 256>(a, 0, a.N - narrow, s);
+    if (narrow > 0) launch_cols<EPI, 128>(a, a.N - narrow, a.N, s);
+}
+
+}  // namespace
+
 hipError_t launch_gemm(const GemmLaunch &a, hipStream_t s) {
     const int tn = gemm_tile_n(a.epi, a.M, a.N);
-    const int tiles_m = (a.M + kTM - 1) / kTM;
-    const int out_tn = (a.epi == PMA_EPI_SWIGLU) ? tn / 2 : tn;
-    const int total = tiles_m * (a.N / out_tn);
-    const int per_xcd = (total + 7) / 8;
-    const dim3 grid(8 * per_xcd);
-    const int nt = kNW * 64;
     switch (a.epi) {
         case PMA_EPI_STORE:
-            if (tn == 224) launch_r<PMA_EPI_STORE, 224>(a, grid, nt, s);
-            else launch_r<PMA_EPI_STORE, 256>(a, grid, nt, s);
+            if (tn == 224) launch_cols<PMA_EPI_STORE, 224>(a, 0, a.N, s);
+            else launch_cols<PMA_EPI_STORE, 256>(a, 0, a.N, s);
             break;
         case PMA_EPI_GATE_RESIDUAL:
-            if (tn == 224) launch_r<PMA_EPI_GATE_RESIDUAL, 224>(a, grid, nt, s);
-            else launch_r<PMA_EPI_GATE_RESIDUAL, 256>(a, grid, nt, s);
+            if (tn == 224) launch_cols<PMA_EPI_GATE_RESIDUAL, 224>(a, 0, a.N, s);
+            else launch_cols<PMA_EPI_GATE_RESIDUAL, 256>(a, 0, a.N, s);
             break;
-        case PMA_EPI_SWIGLU: launch_r<PMA_EPI_SWIGLU, 256>(a, grid, nt, s); break;
-        case kEpiQkvF16: launch_r<kEpiQkvF16, 256>(a, grid, nt, s); break;
-        case kEpiQkvF8: launch_r<kEpiQkvF8, 256>(a, grid, nt, s); break;
+        case PMA_EPI_SWIGLU: launch_cols<PMA_EPI_SWIGLU, 256>(a, 0, a.N, s); break;
+        case kEpiQkvF16: launch_qkv<kEpiQkvF16>(a, s); break;
+        case kEpiQkvF8: launch_qkv<kEpiQkvF8>(a, s); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -121,6 +121,9 @@ struct GemmLaunch {
     const float *wq, *wk;       // norm weights [128]
     const float2 *rope;         // (cos, sin) [L][3F]
     uint16_t *qh, *kh, *vt;     // [H][Lp][128], [H][Lp][128], [H][128][Lp]
+    // output columns [n_begin, n_end) of this launch (n_end 0: all N);
+    // launch_gemm sets them when it splits a problem between tile shapes
+    int32_t n_begin, n_end;
 };
 // internal epilogue id (beside PMA_EPI_*): the fused QKV projection
 constexpr int kEpiQkvRope = 3;
@@ -128,6 +131,9 @@ hipError_t launch_gemm(const GemmLaunch &a, hipStream_t s);
 // W rows per output tile launch_gemm takes for this problem (256, or 224
 // where that fills the last round of tiles better)
 int gemm_tile_n(int epi, int M, int N);
+// output columns the fused QKV projection runs as 128-wide tiles in a second
+// launch (0: none)
+int gemm_qkv_narrow_columns(int M, int N);
 
 struct LnModLaunch {
     int32_t L, hidden, T, shift_chunk;

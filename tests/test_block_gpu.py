@@ -206,6 +206,55 @@ def test_linear_tile_shapes_agree(epi):
     assert not (err > bound).any(), f"worst {err.max()}"
 
 
+def test_qkv_projection_column_split_agrees():
+    """At L = 8192, H = 56, hidden = 5376 the fused QKV projection runs its
+    last 1024 output columns (V heads 48..55) as 128-wide tiles in a second
+    launch (2688 wide tiles are 10.5 rounds on 256 CUs; 2560 wide + 256
+    narrow ones are 10 rounds and one narrow round); at L = 6144 every column
+    runs on 256-wide tiles.  A row's Q', K' and V^T depend only on its own A
+    row and position, and both tile shapes sum over K in the same order, so
+    the first 6144 rows agree bit for bit; V of sampled rows in the narrow
+    columns is checked against fp64."""
+    import torch
+    from packed_masked_attention_amd import binding as B
+    assert torch.cuda.get_device_properties(0).multi_processor_count == 256
+    L, H, hidden, F = 8192, 56, 5376, 16
+    HD = H * 128
+    rng = np.random.default_rng(31)
+    tags = rng.integers(0, 3, L).astype(np.int32)
+    tags[rng.random(L) < 0.05] = -1
+    pos = rng.integers(0, 300, (L, 3)).astype(np.int32)
+    pos[tags == -1] = 0
+    g = torch.Generator(device="cuda").manual_seed(31)
+    a = torch.randn(L, hidden, device="cuda", generator=g).to(torch.bfloat16)
+    w = (torch.randn(3 * HD, hidden, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    wq = torch.rand(128, device="cuda", generator=g) + 0.5
+    wk = torch.rand(128, device="cuda", generator=g) + 0.5
+    p = B.attn_params(H, F=F)
+    out = {}
+    for n in (L, 6144):
+        say(f"qkv projection L={n} H={H} hidden={hidden}")
+        dl = B.pma_layout_build(synth.layout_from_tags(tags[:n], pos[:n], np.zeros(n, np.int32), 1))
+        Lp = B.pma_attention_padded_len(n)
+        rope = torch.empty(n, 3 * F, 2, dtype=torch.float32, device="cuda")
+        qh = torch.full((H, Lp, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+        kh = torch.full_like(qh, float("nan"))
+        vt = torch.full((H, 128, Lp), float("nan"), dtype=torch.bfloat16, device="cuda")
+        B.pma_rope_table(p, dl, rope)
+        B.pma_qkv_projection(p, dl, a, hidden, hidden, w, wq, wk, rope, qh, kh, vt)
+        torch.cuda.synchronize()
+        out[n] = (qh, kh, vt)
+    i16 = lambda t: t.contiguous().view(torch.int16)
+    assert torch.equal(i16(out[L][0][:, :6144]), i16(out[6144][0][:, :6144]))
+    assert torch.equal(i16(out[L][1][:, :6144]), i16(out[6144][1][:, :6144]))
+    assert torch.equal(i16(out[L][2][:, :, :6144]), i16(out[6144][2][:, :, :6144]))
+    # V of the narrow columns (heads 48..55) on sampled rows, among them rows past 6144
+    rows = np.sort(rng.choice(L, 40, replace=False))
+    v_ref = bf16_to_np(a[rows].contiguous()) @ bf16_to_np(w[2 * HD + 48 * 128:].contiguous()).T
+    got = bf16_to_np(out[L][2][48:, :, rows].permute(2, 0, 1).reshape(rows.size, 8 * 128).contiguous())
+    assert np.all(np.abs(got - v_ref) <= one_rounding(v_ref))
+
+
 _one_rounding = one_rounding
 
 
