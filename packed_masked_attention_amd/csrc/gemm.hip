@@ -240,9 +240,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
                       (TN == 128 && (EPI == kEpiQkvF16 || EPI == kEpiQkvF8)),
                   "tile shapes: 224 for the store and gated residual, 128 for the QKV epilogue");
     // five 32 KB slots, each one operand half-stage (256 rows x 64 K): half h
-    // (A of stage s is h = 2s, W of stage s is h = 2s + 1) lives in slot h % 5;
-    // one object per slot, so the compiler can tell the slot being streamed
-    // into from the ones being read
+    // (A of stage s is h = 2s, W of stage s is h = 2s + 1) lives in slot
+    // (h + 2 P0) % 5, P0 the ring's phase offset below; one object per slot,
+    // so the compiler can tell the slot being streamed into from the ones
+    // being read
     __shared__ __attribute__((aligned(1024))) uint16_t h0[kStageElems];
     __shared__ __attribute__((aligned(1024))) uint16_t h1[kStageElems];
     __shared__ __attribute__((aligned(1024))) uint16_t h2[kStageElems];
