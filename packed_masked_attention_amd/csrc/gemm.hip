@@ -47,6 +47,9 @@
 // panels in its L2.  Two more tile shapes fill the CUs' last round better
 // (see Tile below): 256 x 224 for the store and gated-residual epilogues, and
 // 256 x 128 for the last columns of the QKV projection, in a second launch.
+// With the store and SwiGLU epilogues on 256-wide tiles one persistent
+// workgroup per CU runs its XCD's tiles in turn and requests the next tile's
+// first stages before the current tile's epilogue.
 #include "internal.h"
 
 #include <atomic>
@@ -255,27 +258,45 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
     const int l32 = lane & 31, hi = lane >> 5;
     const int wm = wave / WN, wn = wave % WN;
 
-    // ---- tile (XCD-aware, grouped)
+    // ---- tiles (XCD-aware, grouped).  With the store and SwiGLU epilogues on
+    // 256-wide tiles the workgroups are persistent: workgroup b runs the tiles
+    // b/8, b/8 + G/8, ... of XCD b%8's share (G workgroups), and issues the
+    // next tile's first DMA before the current tile's epilogue, whose stores
+    // then overlap the next tile's first stages.  (The gated residual reads R
+    // and the gate in its epilogue, loads that would wait behind that DMA:
+    // 0.5-2% slower persistent, as were the 224-wide store tiles; the QKV
+    // epilogue uses the LDS.)
+    constexpr bool kPersist = TN == 256 && (EPI == PMA_EPI_STORE || EPI == PMA_EPI_SWIGLU);
     const int tiles_m = (a.M + kTM - 1) / kTM;
     const int out_tn = (EPI == PMA_EPI_SWIGLU) ? TN / 2 : TN;
     const int tiles_n = (a.n_end - a.n_begin) / out_tn;   // output columns [n_begin, n_end)
     const int total = tiles_m * tiles_n;
     const int per_xcd = (total + 7) / 8;
-    const int t = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-    if (t >= total) return;
+    const int xcd = (int)(blockIdx.x & 7);
+    int li = (int)(blockIdx.x >> 3);
+    if (li >= per_xcd || xcd * per_xcd + li >= total) return;
     const int per_group = kGroupM * tiles_n;
-    const int group = t / per_group;
-    const int first_m = group * kGroupM;
-    const int gsize = min(kGroupM, tiles_m - first_m);
-    const int tm = first_m + (t % per_group) % gsize;
-    const int tn = (t % per_group) / gsize;
-    const int m0 = tm * kTM;
-    const int n0 = a.n_begin + tn * out_tn;
+    auto tile_of = [&](int l, int &tm0, int &tn0) __attribute__((always_inline)) {
+        const int t = xcd * per_xcd + l;
+        const int group = t / per_group;
+        const int first_m = group * kGroupM;
+        const int gsize = min(kGroupM, tiles_m - first_m);
+        tm0 = (first_m + (t % per_group) % gsize) * kTM;
+        tn0 = a.n_begin + ((t % per_group) / gsize) * out_tn;
+    };
+    int m0, n0;
+    tile_of(li, m0, n0);
 
-    // ---- operand streams.  A rows m0.. (bound: rows < M), W rows per tile row.
-    const uint32_t a_bytes = (uint32_t)(a.M - m0) * (uint32_t)a.lda * 2u;
-    const __amdgpu_buffer_rsrc_t ars = make_rsrc(a.A + (int64_t)m0 * a.lda, a_bytes);
-    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(a.W, a.w_bytes);
+    // ---- operand streams.  A rows m0.. (bound: rows < M), W rows from the
+    // tile's first (the SwiGLU up rows N further on); offsets are relative to
+    // the tile's rows, so only the buffer resources change from tile to tile.
+    auto a_rsrc = [&](int tm0) __attribute__((always_inline)) {
+        return make_rsrc(a.A + (int64_t)tm0 * a.lda, (uint32_t)(a.M - tm0) * (uint32_t)a.lda * 2u);
+    };
+    auto w_rsrc = [&](int tn0) __attribute__((always_inline)) {
+        return make_rsrc(a.W + (int64_t)tn0 * a.ldw, a.w_bytes - (uint32_t)tn0 * (uint32_t)a.ldw * 2u);
+    };
+    __amdgpu_buffer_rsrc_t ars = a_rsrc(m0), wrs = w_rsrc(n0);
     // wave-instruction j of a half fills tile rows 8j..8j+7 (lane l: row
     // 8j + l/8, position l%8, fetching the chunk the swizzle places there);
     // this wave issues j = 8*wave + i (A) and j = NW*wave + i (W) of every
@@ -294,9 +315,9 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
         if (EPI == PMA_EPI_SWIGLU) {
             // W-tile rows 64w..64w+63 = [gate 32w..32w+31 | up 32w..32w+31]
             const int w = r >> 6, rr = r & 63;
-            wrow = n0 + 32 * w + (rr & 31) + ((rr & 32) ? a.N : 0);
+            wrow = 32 * w + (rr & 31) + ((rr & 32) ? a.N : 0);
         } else {
-            wrow = n0 + r;
+            wrow = r;
         }
         wvo[i] = 2u * ((uint32_t)wrow * (uint32_t)a.ldw + 8u * c);
     }
@@ -320,12 +341,6 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
     };
 
     f32x16 acc[FI][FJ];
-#pragma unroll
-    for (int i = 0; i < FI; ++i)
-#pragma unroll
-        for (int j = 0; j < FJ; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     // fragment rows of this lane in the two tiles; fragments of a k-step (16
     // deep) are read one k-step ahead of their MFMAs, across stage ends too,
@@ -400,20 +415,31 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
     constexpr int H = !kHeadPeel ? 0 : R == 0 ? 5 : R;
     constexpr int P0 = (5 - H) % 5;
     // ---- prologue: stages 0 and the A half of 1 requested and the leading
-    // part of the W half of 1 (what k-step 3 of a stage -1 would issue);
+    // part of the W half of 1 (what k-step 3 of a stage -1 would issue)
+    auto prologue = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dma16(ars, (lds_void *)&slot(2 * P0)[(8 * wave + i) * 512], avo[i], 0u);
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+            dma16(wrs, (lds_void *)&slot(2 * P0 + 1)[(NW * wave + i) * 512], wvo[i], 0u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            dma16(ars, (lds_void *)&slot(2 * P0 + 2)[(8 * wave + i) * 512], avo[i],
+                  2u * (uint32_t)(min(1, nk - 1) * kTK));
+#pragma unroll
+        for (int q = 0; q < S::n[0]; ++q) dma_q(0, P0, q);
+    };
+    prologue();
+    for (;;) {
     // stage 0 landed
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(ars, (lds_void *)&slot(2 * P0)[(8 * wave + i) * 512], avo[i], 0u);
-#pragma unroll
-    for (int i = 0; i < NW; ++i) dma16(wrs, (lds_void *)&slot(2 * P0 + 1)[(NW * wave + i) * 512], wvo[i], 0u);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        dma16(ars, (lds_void *)&slot(2 * P0 + 2)[(8 * wave + i) * 512], avo[i],
-              2u * (uint32_t)(min(1, nk - 1) * kTK));
-#pragma unroll
-    for (int q = 0; q < S::n[0]; ++q) dma_q(0, P0, q);
     PMA_STAGE_END(8 + S::n[0]);
     load_frags(slot(2 * P0), slot(2 * P0 + 1), 0, af[0], wf[0]);
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     if constexpr (H > 0) stage(0, P0);
     if constexpr (H > 1) stage(1, P0 + 1);
@@ -436,18 +462,32 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
     }
     // no DMA may still be writing when the slots are reused or released
     PMA_STAGE_END(0);
+    // the next tile's first DMA goes out before this tile's epilogue (which
+    // does not use the LDS)
+    const int cm0 = m0, cn0 = n0;
+    bool more = false;
+    if constexpr (kPersist) {
+        li += (int)(gridDim.x >> 3);
+        more = li < per_xcd && xcd * per_xcd + li < total;
+        if (more) {
+            tile_of(li, m0, n0);
+            ars = a_rsrc(m0);
+            wrs = w_rsrc(n0);
+            prologue();
+        }
+    }
 
     // ---- epilogue.  acc[i][j] register v: output row m0 + (256/WM)*wm + 32*i + l32,
     // W-tile row (TN/WN)*wn + 32*j + 8*(v/4) + 4*hi + v%4.
     if constexpr (EPI == kEpiQkvF16 || EPI == kEpiQkvF8) {
         // the ring is free again (every wave is past the last stage's barrier)
         uint16_t *stg = wave == 0 ? h0 : wave == 1 ? h1 : wave == 2 ? h2 : h3;
-        qkv_epilogue<EPI == kEpiQkvF16 ? 16 : 8, FI>(a, acc, m0, n0, wm, wn, l32, hi, stg);
+        qkv_epilogue<EPI == kEpiQkvF16 ? 16 : 8, FI>(a, acc, cm0, cn0, wm, wn, l32, hi, stg);
         return;
     }
 #pragma unroll
     for (int i = 0; i < FI; ++i) {
-        const int m = m0 + (kTM / T::WM) * wm + 32 * i + l32;
+        const int m = cm0 + (kTM / T::WM) * wm + 32 * i + l32;
         if (m >= a.M) continue;
         uint16_t *crow = a.C + (int64_t)m * a.ldc;
         if constexpr (EPI == PMA_EPI_SWIGLU) {
@@ -457,7 +497,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
             for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int col = n0 + 32 * (2 * wn + jj) + 8 * g + 4 * hi;
+                    const int col = cn0 + 32 * (2 * wn + jj) + 8 * g + 4 * hi;
                     float h[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
@@ -482,7 +522,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
             for (int j = 0; j < FJ; ++j)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int col = n0 + (TN / WN) * wn + 32 * j + 8 * g + 4 * hi;
+                    const int col = cn0 + (TN / WN) * wn + 32 * j + 8 * g + 4 * hi;
                     float y[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * g + e];
@@ -501,6 +541,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
                     *reinterpret_cast<uint2 *>(crow + col) = w;
                 }
         }
+    }
+    if (!more) break;
     }
 }
 
@@ -571,7 +613,10 @@ void launch_cols(const GemmLaunch &a, int n_begin, int n_end, hipStream_t s) {
     const int out_tn = (EPI == PMA_EPI_SWIGLU) ? TN / 2 : TN;
     const int total = tiles_m * ((n_end - n_begin) / out_tn);
     const int per_xcd = (total + 7) / 8;
-    launch_r<EPI, TN>(b, dim3(8 * per_xcd), kNW * 64, s);
+    // persistent epilogues: one workgroup per CU (the LDS admits one)
+    const bool persist = TN == 256 && (EPI == PMA_EPI_STORE || EPI == PMA_EPI_SWIGLU);
+    const int per_xcd_wg = persist ? min(per_xcd, max(1, device_cus() / 8)) : per_xcd;
+    launch_r<EPI, TN>(b, dim3(8 * per_xcd_wg), kNW * 64, s);
 }
 
 template <int EPI>
