@@ -90,7 +90,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcFlags);
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z), with the hardware reciprocal (1 ulp) instead of an
+// IEEE division: the product is rounded to bf16 (2^-9) right after, and the
+// division's scale-and-fixup sequence was most of the SwiGLU epilogue's VALU
+// work.  e^-z = inf gives z * 0 (the limit), e^-z = 0 gives z.
+__device__ __forceinline__ float silu(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // QKV_ROPE epilogue ids: one per rope_freq_dim F (the partner of a rotated
 // channel sits F/2 accumulator registers away in the same lane)
