@@ -9,62 +9,59 @@
 // padding rows (tag -1) use zero modulation; without a table (the token
 // refiner's output norm) every row is normalised only.
 //
-// HBM-bound: one 256-thread block per row reads the row once (kept in
-// registers for both passes of the mean/variance), gathers the two fp32
-// modulation rows (3 x T distinct rows, L2-resident) and writes the row once.
+// HBM-bound: one wave per row reads the row once (kept in registers for both
+// passes of the mean/variance), gathers the two fp32 modulation rows (3 x T
+// distinct rows, L2-resident) and writes the row once.
 #include "internal.h"
 
 namespace pma {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxChunks = 4;   // 16-byte chunks per thread: hidden <= 256*8*4 = 8192
+constexpr int kRowsPerBlock = kThreads / 64;   // one wave per row
+constexpr int kMaxChunks = 16;  // 16-byte chunks per lane: hidden <= 64*8*16 = 8192
 
-__device__ __forceinline__ float block_sum(float v, float *red) {
+__device__ __forceinline__ float wave_sum(float v) {
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    __syncthreads();
-    if (lane == 0) red[wave] = v;
-    __syncthreads();
-    float t = 0.f;
-#pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) t += red[w];
-    return t;
+    return v;
 }
 
+// One wave per row, CPL 16-byte chunks per lane (hidden <= 512 CPL): the row
+// stays in registers as bf16 for both passes of the mean/variance, and the
+// reductions stay inside the wave (no block barriers; 46 -> 43 us at
+// 8192 x 5376 against one 256-thread block per row).
+template <int CPL>
 __global__ __launch_bounds__(kThreads) void ln_modulate_kernel(LnModLaunch a) {
-    __shared__ float red[kThreads / 64];
-    const int row = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= a.L) return;
     const int nchunk = a.hidden / 8;
     const uint16_t *xr = a.x + (int64_t)row * a.hidden;
-    float v[kMaxChunks][8];
+    u16x8 raw[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = lane + 64 * i;
+        raw[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (c < nchunk) raw[i] = *reinterpret_cast<const u16x8 *>(xr + 8 * c);
+    }
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < kMaxChunks; ++i) {
-        const int c = threadIdx.x + i * kThreads;
-        if (c < nchunk) {
-            const u16x8 raw = *reinterpret_cast<const u16x8 *>(xr + 8 * c);
+    for (int i = 0; i < CPL; ++i)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                v[i][t] = bf16_bits_to_f32(raw[t]);
-                s += v[i][t];
-            }
-        }
-    }
-    const float mean = block_sum(s, red) / (float)a.hidden;
+        for (int t = 0; t < 8; ++t) s += bf16_bits_to_f32(raw[i][t]);
+    const float mean = wave_sum(s) / (float)a.hidden;
     float q = 0.f;
 #pragma unroll
-    for (int i = 0; i < kMaxChunks; ++i) {
-        const int c = threadIdx.x + i * kThreads;
-        if (c < nchunk) {
+    for (int i = 0; i < CPL; ++i) {
+        if (lane + 64 * i < nchunk) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const float d = v[i][t] - mean;
+                const float d = bf16_bits_to_f32(raw[i][t]) - mean;
                 q = fmaf(d, d, q);
             }
         }
     }
-    const float var = block_sum(q, red) / (float)a.hidden;
+    const float var = wave_sum(q) / (float)a.hidden;
     const float rstd = 1.0f / sqrtf(var + a.eps);
     const int tag = a.tags[row], ts = a.ts_idx[row];
     const float *shift = nullptr, *scale = nullptr;
@@ -75,8 +72,8 @@ __global__ __launch_bounds__(kThreads) void ln_modulate_kernel(LnModLaunch a) {
     }
     uint16_t *orow = a.out + (int64_t)row * a.hidden;
 #pragma unroll
-    for (int i = 0; i < kMaxChunks; ++i) {
-        const int c = threadIdx.x + i * kThreads;
+    for (int i = 0; i < CPL; ++i) {
+        const int c = lane + 64 * i;
         if (c < nchunk) {
             float y[8];
             if (shift) {
@@ -86,12 +83,12 @@ __global__ __launch_bounds__(kThreads) void ln_modulate_kernel(LnModLaunch a) {
                 const f32x4 sc1 = *reinterpret_cast<const f32x4 *>(scale + 8 * c + 4);
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    y[t] = fmaf((v[i][t] - mean) * rstd, 1.0f + sc0[t], sh0[t]);
-                    y[t + 4] = fmaf((v[i][t + 4] - mean) * rstd, 1.0f + sc1[t], sh1[t]);
+                    y[t] = fmaf((bf16_bits_to_f32(raw[i][t]) - mean) * rstd, 1.0f + sc0[t], sh0[t]);
+                    y[t + 4] = fmaf((bf16_bits_to_f32(raw[i][t + 4]) - mean) * rstd, 1.0f + sc1[t], sh1[t]);
                 }
             } else {
 #pragma unroll
-                for (int t = 0; t < 8; ++t) y[t] = (v[i][t] - mean) * rstd;
+                for (int t = 0; t < 8; ++t) y[t] = (bf16_bits_to_f32(raw[i][t]) - mean) * rstd;
             }
             uint4 w;
             w.x = pack_bf16x2(y[0], y[1]);
@@ -106,10 +103,15 @@ __global__ __launch_bounds__(kThreads) void ln_modulate_kernel(LnModLaunch a) {
 }  // namespace
 
 hipError_t launch_ln_modulate(const LnModLaunch &a, hipStream_t s) {
-    ln_modulate_kernel<<<a.L, kThreads, 0, s>>>(a);
+    const dim3 grid((a.L + kRowsPerBlock - 1) / kRowsPerBlock);
+    const int cpl = (a.hidden / 8 + 63) / 64;
+    if (cpl <= 4) ln_modulate_kernel<4><<<grid, kThreads, 0, s>>>(a);
+    else if (cpl <= 8) ln_modulate_kernel<8><<<grid, kThreads, 0, s>>>(a);
+    else if (cpl <= 12) ln_modulate_kernel<12><<<grid, kThreads, 0, s>>>(a);
+    else ln_modulate_kernel<16><<<grid, kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 
-int ln_modulate_max_hidden() { return kThreads * 8 * kMaxChunks; }
+int ln_modulate_max_hidden() { return 64 * 8 * kMaxChunks; }
 
 }  // namespace pma
