@@ -29,6 +29,11 @@ L=8192: timestep MLP, head table, token refiner (2 blocks on the 512 text
 rows), pack, the 50-block stack and the output heads; value is its
 algorithmic TFLOP/s, and a HIP graph of the same step is timed beside it.
 
+With --workload gate_ln_L8192 the block's O-projection + gated residual and
+the pre-FFN LN-modulate are timed two ways, interleaved: as the block runs
+them (two launches) and as pma_gate_residual_ln_modulate (the norm
+statistics taken in the projection's epilogue); value is the first, in us.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--copy-probe BYTES]
 """
@@ -692,6 +697,87 @@ def forward_bench(args) -> int:
     return 0
 
 
+def gate_ln_bench(args) -> int:
+    """The block's a7 + a8 pair at L=8192 two ways, interleaved on one GPU:
+    the O-projection with the gated residual, then the LN-modulate pass (the
+    block's path), against pma_gate_residual_ln_modulate (the same
+    projection also taking each rounded row's norm statistics in its
+    epilogue, the norm pass reading them instead of reducing the row)."""
+    import numpy as np
+    import torch
+    from packed_masked_attention_amd import binding as B
+    from packed_masked_attention_amd import synth
+
+    torch.cuda.set_device(0)
+    wl = synth.workload("block_L8192")
+    lay = synth.layout_from_counts(wl.text, wl.video, wl.audio, wl.pad, wl.T)
+    L, N, K, T = wl.L, wl.hidden, wl.H * wl.D, lay["T"]
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed)
+    rnd = lambda *shape, std=1.0: (std * torch.randn(*shape, device=dev, generator=g)).to(torch.bfloat16)
+    A, W, x = rnd(L, K), rnd(N, K, std=wl.weight_std), rnd(L, N)
+    table = torch.randn(3, T, 6, N, device=dev, generator=g)
+    p = B.block_params(N, wl.ffn, wl.temb_dim, wl.H)
+    dl = B.pma_layout_build(lay, device=dev)
+    tags = torch.from_numpy(lay["tags"]).to(dev)
+    ts = torch.from_numpy(lay["ts_idx"]).to(dev)
+    x1, b = torch.empty_like(x), torch.empty_like(x)
+    ws = torch.empty(B.pma_gate_ln_workspace_size(p, L), dtype=torch.uint8, device=dev)
+
+    def unfused():
+        B.pma_linear(L, N, K, A, K, W, K, x1, N, B.EPI_GATE_RESIDUAL, R=x, ldr=N, table=table,
+                     num_timesteps=T, gate_chunk=2, tags=tags, ts_idx=ts)
+        B.pma_ln_modulate(p, dl, table, 1, x1, b)
+
+    def fused():
+        B.pma_gate_residual_ln_modulate(p, dl, A, K, K, W, table, 2, x, x1, table, 1, b, ws)
+
+    def norm_only():
+        B.pma_ln_modulate(p, dl, table, 1, x1, b)
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    cases = {"unfused": unfused, "fused": fused, "norm_only": norm_only}
+    for fn in cases.values():
+        for _ in range(args.warmup):
+            fn()
+    torch.cuda.synchronize()
+    reps = 5
+    us = {k: [] for k in cases}
+    t0 = time.perf_counter()
+    for r in range(reps):
+        for k, fn in cases.items():
+            us[k].append(timed(fn, args.steps))
+        log(f"[bench] rep {r}: " + ", ".join(f"{k} {v[-1]:.1f} us" for k, v in us.items()))
+    wall = time.perf_counter() - t0
+    med = {k: float(np.median(v)) for k, v in us.items()}
+    flops = 2.0 * L * N * K
+    out = {
+        "metric": "O-projection + gated residual + pre-FFN LN-modulate time at L=8192",
+        "value": round(med["unfused"], 1), "unit": "us", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(med["unfused"] / 1e3, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gate_ln_L8192", "seq_len": L, "hidden": N, "K": K,
+                   "step": "x1 = x + gate_a (O W_o^T); b = LN(x1)(1 + scale_f) + shift_f",
+                   "reps": reps, "wall_s": round(wall, 2)},
+        "median_us": {k: round(v, 1) for k, v in med.items()},
+        "fused_minus_unfused_us": round(med["fused"] - med["unfused"], 1),
+        "projection_tflops_unfused_pair": round(flops / (med["unfused"] * 1e-6) / 1e12, 1),
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -720,6 +806,8 @@ def main() -> int:
         return io_bench(args)
     if args.workload == "forward_L8192":
         return forward_bench(args)
+    if args.workload == "gate_ln_L8192":
+        return gate_ln_bench(args)
 
     import numpy as np
     import torch

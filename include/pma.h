@@ -351,6 +351,39 @@ typedef struct {
  * byte offsets (< 4 GiB).  Rows >= M are neither read nor written. */
 pma_status pma_linear(const pma_linear_args *args, void *stream);
 
+/* Device workspace of pma_gate_residual_ln_modulate for seq_len rows (the
+ * rows' LayerNorm statistics: at most hidden / 128 fp32 pairs per row). */
+pma_status pma_gate_ln_workspace_size(const pma_block_params *p, int32_t seq_len,
+                                      size_t *bytes);
+
+/* A gated residual fused with the next AdaLN norm.  [ENG] "Exacte DiT
+ * fusions": the attention residual gate is fused with the following MLP
+ * AdaLN, and the rounded row stays on chip for its norm.  Here:
+ *   x1 = x + gate * (a w^T), rounded to bf16 once (pma_linear with the
+ *        GATE_RESIDUAL epilogue, gate = gate_table chunk gate_chunk, 2 =
+ *        gate_a or 5 = gate_f), whose epilogue also takes, from the rounded
+ *        values in its registers, each row's mean and sum of squared
+ *        deviations over the columns one wave holds (two passes);
+ *   b  = LN(x1) * (1 + scale) + shift as pma_ln_modulate with mod_table and
+ *        which, its mean and variance combined from those per-group pairs
+ *        (Chan's pairwise update) instead of a reduction over the row.
+ * x1 is bit-identical to pma_linear's GATE_RESIDUAL output; b equals
+ * pma_ln_modulate(x1) up to the fp32 summation order of the statistics.
+ * a: bf16 [L][K] (leading dimension lda), w: bf16 [hidden][K], x, x1, b:
+ * bf16 [L][hidden] (x1 may alias x, b may alias x1); K % 64 == 0.  The two
+ * tables may differ (the block's a7 -> a8 uses one table with gate_chunk 2
+ * and which 1; a block's fc2 and the next block's first norm, gate_chunk 5
+ * and which 0 with the next block's table).  workspace: at least
+ * pma_gate_ln_workspace_size bytes, 256-byte aligned; it holds the
+ * statistics between the two launches, so calls that share it must not
+ * overlap. */
+pma_status pma_gate_residual_ln_modulate(const pma_block_params *p, const pma_layout *layout,
+                                         const pma_bf16 *a, int64_t lda, int32_t K,
+                                         const pma_bf16 *w, const float *gate_table,
+                                         int32_t gate_chunk, const pma_bf16 *x, pma_bf16 *x1,
+                                         const float *mod_table, int32_t which, pma_bf16 *b,
+                                         void *workspace, size_t workspace_bytes, void *stream);
+
 /* (cos, sin) of every row's rotation angles for the fused QKV projection:
  * table fp32 [L][3F][2], entry [i][a*F + f] = (cos, sin) of
  * pos[i][a] * theta^(-f/F) (the angle of the attention section's RoPE),

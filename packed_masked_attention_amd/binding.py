@@ -117,6 +117,11 @@ _SIGS = {
     "pma_ln_modulate": (_i32, [ctypes.POINTER(BlockParams), ctypes.POINTER(Layout), _vp, _i32,
                                _vp, _vp, _vp]),
     "pma_linear": (_i32, [ctypes.POINTER(LinearArgs), _vp]),
+    "pma_gate_ln_workspace_size": (_i32, [ctypes.POINTER(BlockParams), _i32,
+                                          ctypes.POINTER(ctypes.c_size_t)]),
+    "pma_gate_residual_ln_modulate": (_i32, [ctypes.POINTER(BlockParams), ctypes.POINTER(Layout),
+                                             _vp, _i64, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32,
+                                             _vp, _vp, ctypes.c_size_t, _vp]),
     "pma_rope_table": (_i32, [ctypes.POINTER(AttnParams), ctypes.POINTER(Layout), _vp, _vp]),
     "pma_qkv_projection": (_i32, [ctypes.POINTER(AttnParams), ctypes.POINTER(Layout), _vp, _i64,
                                   _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -377,6 +382,25 @@ def pma_linear(M, N, K, A, lda, W, ldw, C, ldc, epilogue=EPI_STORE, R=None, ldr=
     args = LinearArgs(M, N, K, ptr(A), lda, ptr(W), ldw, ptr(C), ldc, epilogue, ptr(R), ldr,
                       ptr(table), num_timesteps, gate_chunk, ptr(tags), ptr(ts_idx))
     check(lib().pma_linear(ctypes.byref(args), stream_ptr(stream)))
+
+
+def pma_gate_ln_workspace_size(p: BlockParams, seq_len: int) -> int:
+    n = ctypes.c_size_t()
+    check(lib().pma_gate_ln_workspace_size(ctypes.byref(p), seq_len, ctypes.byref(n)))
+    return n.value
+
+
+def pma_gate_residual_ln_modulate(p: BlockParams, dl: DeviceLayout, a, lda: int, K: int, w,
+                                  gate_table, gate_chunk: int, x, x1, mod_table, which: int, b,
+                                  workspace=None, stream=None) -> None:
+    import torch
+    if workspace is None:
+        workspace = torch.empty(pma_gate_ln_workspace_size(p, dl.seq_len), dtype=torch.uint8,
+                                device=x.device)
+    check(lib().pma_gate_residual_ln_modulate(
+        ctypes.byref(p), ctypes.byref(dl.struct), ptr(a), lda, K, ptr(w), ptr(gate_table),
+        gate_chunk, ptr(x), ptr(x1), ptr(mod_table), which, ptr(b), ptr(workspace),
+        workspace.numel(), stream_ptr(stream)))
 
 
 def pma_block_workspace_size(p: BlockParams, seq_len: int) -> int:

@@ -95,11 +95,19 @@ pma_status pma_ln_modulate(const pma_block_params *p, const pma_layout *layout,
     a.table = table;
     a.tags = layout->token_tags;
     a.ts_idx = layout->timestep_indices;
+    a.stats = nullptr;
+    a.stats_groups = a.stats_gw = 0;
     CHECK_HIP(launch_ln_modulate(a, static_cast<hipStream_t>(stream)), "ln_modulate launch");
     return PMA_OK;
 }
 
-pma_status pma_linear(const pma_linear_args *g, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// pma_linear; with stats (GATE_RESIDUAL only) the epilogue also writes the
+// rounded rows' statistics, stats_groups pairs per row.
+pma_status linear_impl(const pma_linear_args *g, float2 *stats, int32_t stats_groups, void *stream) {
     if (!g) FAIL(PMA_ERR_NULL, "args are NULL");
     if (g->epilogue < PMA_EPI_STORE || g->epilogue > PMA_EPI_SWIGLU)
         FAIL(PMA_ERR_SHAPE, "epilogue %d", g->epilogue);
@@ -136,7 +144,78 @@ pma_status pma_linear(const pma_linear_args *g, void *stream) {
     a.R = g->R; a.ldr = g->ldr;
     a.table = g->table; a.T = g->num_timesteps; a.gate_chunk = g->gate_chunk;
     a.tags = g->token_tags; a.ts_idx = g->timestep_indices;
+    if (stats) {
+        a.epi = kEpiGateStats;
+        a.stats = stats;
+        a.stats_groups = stats_groups;
+    }
     CHECK_HIP(launch_gemm(a, static_cast<hipStream_t>(stream)), "gemm launch");
+    return PMA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pma_status pma_linear(const pma_linear_args *g, void *stream) { return linear_impl(g, nullptr, 0, stream); }
+
+pma_status pma_gate_ln_workspace_size(const pma_block_params *p, int32_t seq_len, size_t *bytes) {
+    pma_status st;
+    if ((st = check_block_params(p)) != PMA_OK) return st;
+    if (!bytes) FAIL(PMA_ERR_NULL, "bytes is NULL");
+    if (seq_len < 1 || seq_len > (1 << 24)) FAIL(PMA_ERR_SHAPE, "seq_len %d", seq_len);
+    // at most hidden / 128 groups per row (the narrower group width)
+    *bytes = round_up((size_t)seq_len * (size_t)(p->hidden / 128) * sizeof(float2), 256);
+    return PMA_OK;
+}
+
+pma_status pma_gate_residual_ln_modulate(const pma_block_params *p, const pma_layout *layout,
+                                         const pma_bf16 *a_in, int64_t lda, int32_t K,
+                                         const pma_bf16 *w, const float *gate_table,
+                                         int32_t gate_chunk, const pma_bf16 *x, pma_bf16 *x1,
+                                         const float *mod_table, int32_t which, pma_bf16 *b,
+                                         void *workspace, size_t workspace_bytes, void *stream) {
+    pma_status st;
+    if ((st = check_block_params(p)) != PMA_OK) return st;
+    if (!layout || !layout->token_tags || !layout->timestep_indices)
+        FAIL(PMA_ERR_NULL, "layout is not built");
+    if (!mod_table || !b || !workspace) FAIL(PMA_ERR_NULL, "mod_table, b and workspace are required");
+    if (which != 0 && which != 1) FAIL(PMA_ERR_SHAPE, "which %d (0 or 1)", which);
+    if (gate_chunk != 2 && gate_chunk != 5) FAIL(PMA_ERR_SHAPE, "gate_chunk %d (2 or 5)", gate_chunk);
+    if (!aligned(b, 16) || !aligned(mod_table, 16) || !aligned(workspace, 256))
+        FAIL(PMA_ERR_ALIGN, "b, mod_table 16-byte and workspace 256-byte aligned");
+    const int32_t L = layout->seq_len, hid = p->hidden;
+    size_t need = 0;
+    if ((st = pma_gate_ln_workspace_size(p, L, &need)) != PMA_OK) return st;
+    if (workspace_bytes < need) FAIL(PMA_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+    const int gw = gemm_stats_group_width(L, hid);
+    float2 *stats = static_cast<float2 *>(workspace);
+    // x1 = x + gate (a w^T), rounded, with each row's statistics per group
+    pma_linear_args g;
+    memset(&g, 0, sizeof g);
+    g.M = L; g.N = hid; g.K = K;
+    g.A = a_in; g.lda = lda; g.W = w; g.ldw = K; g.C = x1; g.ldc = hid;
+    g.epilogue = PMA_EPI_GATE_RESIDUAL;
+    g.R = x; g.ldr = hid; g.table = gate_table; g.num_timesteps = layout->num_timesteps;
+    g.gate_chunk = gate_chunk; g.token_tags = layout->token_tags;
+    g.timestep_indices = layout->timestep_indices;
+    if ((st = linear_impl(&g, stats, hid / gw, stream)) != PMA_OK) return st;
+    // b = LN(x1) (1 + scale) + shift from those statistics
+    LnModLaunch m;
+    m.L = L;
+    m.hidden = hid;
+    m.T = layout->num_timesteps;
+    m.shift_chunk = which ? 3 : 0;
+    m.eps = p->norm_eps;
+    m.x = x1;
+    m.out = b;
+    m.table = mod_table;
+    m.tags = layout->token_tags;
+    m.ts_idx = layout->timestep_indices;
+    m.stats = stats;
+    m.stats_groups = hid / gw;
+    m.stats_gw = gw;
+    CHECK_HIP(launch_ln_modulate(m, static_cast<hipStream_t>(stream)), "ln_modulate launch");
     return PMA_OK;
 }
 
@@ -272,7 +351,10 @@ pma_status block_forward_impl(const pma_block_params *p, const pma_layout *layou
                                   stream)) != PMA_OK)
         return st;
     pma_linear_args g;
-    // x1 = x + gate_a (O W_o^T)
+    // x1 = x + gate_a (O W_o^T).  (pma_gate_residual_ln_modulate would take
+    // x1's row statistics in this epilogue for the norm below; measured at
+    // L = 8192 it is 0.8% slower than the two launches: the norm pass already
+    // streams at the device-copy rate, and the statistics cost the epilogue.)
     memset(&g, 0, sizeof g);
     g.M = L; g.N = hid; g.K = (int32_t)HD;
     g.A = o; g.lda = HD; g.W = w->w_o; g.ldw = HD; g.C = x1; g.ldc = hid;

@@ -10,6 +10,13 @@
 // Epilogues fused into the store:
 //   STORE          C = acc                                (plain projection)
 //   GATE_RESIDUAL  C = R + gate[tag, ts] * acc            (O-projection, fc2)
+//   GATE_STATS     GATE_RESIDUAL, and per row the LayerNorm statistics of
+//                  the rounded C row over the columns a wave holds (its mean
+//                  and sum of squared deviations, two passes over registers),
+//                  so the next norm needs no reduction over the row.
+//                  Page "MiniMax H3 Inference Engine voor Mac computers",
+//                  "Exacte DiT fusions": the residual gate fused with the
+//                  next AdaLN, the rounded row kept on chip for its norm.
 //   SWIGLU         C = silu(acc over gate rows) * acc over the matching up rows (fc1)
 //   QKV_ROPE       the QKV projection straight into the attention operands: the
 //                  Q and K columns are RMS-normalised per (row, head) and
@@ -216,6 +223,14 @@ __device__ __forceinline__ void qkv_epilogue(const GemmLaunch &a, f32x16 (&acc)[
 // (64 rows x all 224 W rows), for N where 224-wide tiles fill the CUs'
 // last round of tiles better (N = 5376: 768 tiles, three full rounds on 256
 // CUs, against 672 = 2.625 rounds of 256-wide tiles).
+// Sum of a value over the lane pair (l, l ^ 32): v_permlane32_swap leaves
+// {own, partner} in the two results.
+__device__ __forceinline__ float pair_sum(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int TN> struct Tile;
 template <> struct Tile<256> { static constexpr int WM = 2, FI = 4, FJ = 4; };
 template <> struct Tile<224> { static constexpr int WM = 4, FI = 2, FJ = 7; };
@@ -245,7 +260,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
     using S = Sched<TN>;
     constexpr int FI = T::FI, FJ = T::FJ, NW = S::NW;
     constexpr int WN = kNW / T::WM;
-    static_assert(TN == 256 || (TN == 224 && (EPI == PMA_EPI_STORE || EPI == PMA_EPI_GATE_RESIDUAL)) ||
+    constexpr bool kGate = EPI == PMA_EPI_GATE_RESIDUAL || EPI == kEpiGateStats;
+    static_assert(TN == 256 || (TN == 224 && (EPI == PMA_EPI_STORE || kGate)) ||
                       (TN == 128 && (EPI == kEpiQkvF16 || EPI == kEpiQkvF8)),
                   "tile shapes: 224 for the store and gated residual, 128 for the QKV epilogue");
     // five 32 KB slots, each one operand half-stage (256 rows x 64 K): half h
@@ -516,7 +532,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
         } else {
             const float *grow = nullptr;
             const uint16_t *rrow = nullptr;
-            if (EPI == PMA_EPI_GATE_RESIDUAL) {
+            if (kGate) {
                 const int tag = a.tags[m], ts = a.ts_idx[m];
                 rrow = a.R + (int64_t)m * a.ldr;
                 // rows outside the table (padding, or an index a layout check
@@ -532,7 +548,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
                     float y[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * g + e];
-                    if (EPI == PMA_EPI_GATE_RESIDUAL) {
+                    if (kGate) {
                         const uint2 rv = *reinterpret_cast<const uint2 *>(rrow + col);
                         float r4[4] = {bf16_bits_to_f32(rv.x & 0xffff), bf16_bits_to_f32(rv.x >> 16),
                                        bf16_bits_to_f32(rv.y & 0xffff), bf16_bits_to_f32(rv.y >> 16)};
@@ -545,7 +561,37 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_kernel(GemmLaunch a) {
                     w.x = pack_bf16x2(y[0], y[1]);
                     w.y = pack_bf16x2(y[2], y[3]);
                     *reinterpret_cast<uint2 *>(crow + col) = w;
+                    if constexpr (EPI == kEpiGateStats) {
+                        // keep the rounded values (what the next norm reads)
+                        acc[i][j][4 * g] = bf16_bits_to_f32(w.x & 0xffff);
+                        acc[i][j][4 * g + 1] = bf16_bits_to_f32(w.x >> 16);
+                        acc[i][j][4 * g + 2] = bf16_bits_to_f32(w.y & 0xffff);
+                        acc[i][j][4 * g + 3] = bf16_bits_to_f32(w.y >> 16);
+                    }
                 }
+            if constexpr (EPI == kEpiGateStats) {
+                // the row's TN / WN columns of this wave: FJ * 16 in this lane,
+                // as many in lane l ^ 32.  Mean first, then the squared
+                // deviations from it (four independent chains each).
+                constexpr int GW = TN / WN;
+                float c4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < FJ; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) c4[v & 3] += acc[i][j][v];
+                const float mean = pair_sum((c4[0] + c4[1]) + (c4[2] + c4[3])) * (1.0f / GW);
+                float q4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < FJ; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const float d = acc[i][j][v] - mean;
+                        q4[v & 3] = fmaf(d, d, q4[v & 3]);
+                    }
+                const float m2 = pair_sum((q4[0] + q4[1]) + (q4[2] + q4[3]));
+                if (hi == 0)
+                    a.stats[(int64_t)m * a.stats_groups + (cn0 - a.n_begin) / GW + wn] = make_float2(mean, m2);
+            }
         }
     }
     if (!more) break;
@@ -579,7 +625,8 @@ int device_cus() {
 }  // namespace
 
 int gemm_tile_n(int epi, int M, int N) {
-    if ((epi != PMA_EPI_STORE && epi != PMA_EPI_GATE_RESIDUAL) || N % 224 != 0) return 256;
+    if ((epi != PMA_EPI_STORE && epi != PMA_EPI_GATE_RESIDUAL && epi != kEpiGateStats) || N % 224 != 0)
+        return 256;
     // rounds of tiles over the CUs, each round as long as its tiles are wide;
     // the narrower tile is taken when it saves at least 5%
     const int64_t cus = device_cus();
@@ -587,6 +634,12 @@ int gemm_tile_n(int epi, int M, int N) {
     const int64_t r256 = (tiles_m * (N / 256) + cus - 1) / cus;
     const int64_t r224 = (tiles_m * (N / 224) + cus - 1) / cus;
     return r224 * 224 * 100 < r256 * 256 * 95 ? 224 : 256;
+}
+
+int gemm_stats_group_width(int M, int N) {
+    // a wave of a 224-wide tile holds a row's 224 columns; of a 256-wide
+    // tile (2 x 2 waves), 128 of them
+    return gemm_tile_n(kEpiGateStats, M, N) == 224 ? 224 : 128;
 }
 
 int gemm_qkv_narrow_columns(int M, int N) {
@@ -644,6 +697,10 @@ hipError_t launch_gemm(const GemmLaunch &a, hipStream_t s) {
         case PMA_EPI_GATE_RESIDUAL:
             if (tn == 224) launch_cols<PMA_EPI_GATE_RESIDUAL, 224>(a, 0, a.N, s);
             else launch_cols<PMA_EPI_GATE_RESIDUAL, 256>(a, 0, a.N, s);
+            break;
+        case kEpiGateStats:
+            if (tn == 224) launch_cols<kEpiGateStats, 224>(a, 0, a.N, s);
+            else launch_cols<kEpiGateStats, 256>(a, 0, a.N, s);
             break;
         case PMA_EPI_SWIGLU: launch_cols<PMA_EPI_SWIGLU, 256>(a, 0, a.N, s); break;
         case kEpiQkvF16: launch_qkv<kEpiQkvF16>(a, s); break;

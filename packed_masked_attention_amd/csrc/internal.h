@@ -124,9 +124,20 @@ struct GemmLaunch {
     // output columns [n_begin, n_end) of this launch (n_end 0: all N);
     // launch_gemm sets them when it splits a problem between tile shapes
     int32_t n_begin, n_end;
+    // gated residual with row statistics (kEpiGateStats): per row and column
+    // group of gemm_stats_group_width columns, (mean, sum of squared
+    // deviations) of the bf16-rounded output row, [M][stats_groups]
+    float2 *stats;
+    int32_t stats_groups;
 };
-// internal epilogue id (beside PMA_EPI_*): the fused QKV projection
+// internal epilogue ids (beside PMA_EPI_*): the fused QKV projection (3, 4:
+// one per rope_freq_dim), and the gated residual that also takes the
+// LayerNorm statistics of its rounded output rows
 constexpr int kEpiQkvRope = 3;
+constexpr int kEpiGateStats = 5;
+// Columns per row-statistics group of the kEpiGateStats epilogue (the
+// columns one wave of an output tile holds for a row): 224 or 128.
+int gemm_stats_group_width(int M, int N);
 hipError_t launch_gemm(const GemmLaunch &a, hipStream_t s);
 // W rows per output tile launch_gemm takes for this problem (256, or 224
 // where that fills the last round of tiles better)
@@ -142,6 +153,11 @@ struct LnModLaunch {
     uint16_t *out;
     const float *table;
     const int32_t *tags, *ts_idx;
+    // with stats: the rows' statistics from the kEpiGateStats epilogue
+    // (stats_groups groups of stats_gw columns per row) replace the row
+    // reductions
+    const float2 *stats;
+    int32_t stats_groups, stats_gw;
 };
 hipError_t launch_ln_modulate(const LnModLaunch &a, hipStream_t s);
 int ln_modulate_max_hidden();

@@ -11,7 +11,13 @@
 //
 // HBM-bound: one wave per row reads the row once (kept in registers for both
 // passes of the mean/variance), gathers the two fp32 modulation rows (3 x T
-// distinct rows, L2-resident) and writes the row once.
+// distinct rows, L2-resident) and writes the row once.  After a gated
+// residual that took the row statistics in its epilogue (page "MiniMax H3
+// Inference Engine voor Mac computers", "Exacte DiT fusions": the residual
+// gate fused with the next AdaLN), the mean and variance come from those
+// per-group (mean, sum of squared deviations) pairs instead, combined with
+// the pairwise update of Chan, Golub and LeVeque (equal group sizes n_g):
+// mean = sum mean_g / G, M2 = sum (M2_g + n_g (mean_g - mean)^2).
 #include "internal.h"
 
 namespace pma {
@@ -30,7 +36,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 // stays in registers as bf16 for both passes of the mean/variance, and the
 // reductions stay inside the wave (no block barriers; 46 -> 43 us at
 // 8192 x 5376 against one 256-thread block per row).
-template <int CPL>
+template <int CPL, bool STATS>
 __global__ __launch_bounds__(kThreads) void ln_modulate_kernel(LnModLaunch a) {
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
@@ -44,24 +50,36 @@ __global__ __launch_bounds__(kThreads) void ln_modulate_kernel(LnModLaunch a) {
         raw[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
         if (c < nchunk) raw[i] = *reinterpret_cast<const u16x8 *>(xr + 8 * c);
     }
-    float s = 0.f;
+    float mean, var;
+    if constexpr (STATS) {
+        // lane g < G holds group g's pair (G <= 64: hidden <= 8192, groups of
+        // at least 128 columns)
+        float2 st = make_float2(0.f, 0.f);
+        if (lane < a.stats_groups) st = a.stats[(int64_t)row * a.stats_groups + lane];
+        mean = wave_sum(st.x) / (float)a.stats_groups;
+        const float d = st.x - mean;
+        const float m2 = lane < a.stats_groups ? fmaf((float)a.stats_gw * d, d, st.y) : 0.f;
+        var = wave_sum(m2) / (float)a.hidden;
+    } else {
+        float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i)
+        for (int i = 0; i < CPL; ++i)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) s += bf16_bits_to_f32(raw[i][t]);
-    const float mean = wave_sum(s) / (float)a.hidden;
-    float q = 0.f;
+            for (int t = 0; t < 8; ++t) s += bf16_bits_to_f32(raw[i][t]);
+        mean = wave_sum(s) / (float)a.hidden;
+        float q = 0.f;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        if (lane + 64 * i < nchunk) {
+        for (int i = 0; i < CPL; ++i) {
+            if (lane + 64 * i < nchunk) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const float d = bf16_bits_to_f32(raw[i][t]) - mean;
-                q = fmaf(d, d, q);
+                for (int t = 0; t < 8; ++t) {
+                    const float d = bf16_bits_to_f32(raw[i][t]) - mean;
+                    q = fmaf(d, d, q);
+                }
             }
         }
+        var = wave_sum(q) / (float)a.hidden;
     }
-    const float var = wave_sum(q) / (float)a.hidden;
     const float rstd = 1.0f / sqrtf(var + a.eps);
     const int tag = a.tags[row], ts = a.ts_idx[row];
     const float *shift = nullptr, *scale = nullptr;
@@ -105,10 +123,19 @@ __global__ __launch_bounds__(kThreads) void ln_modulate_kernel(LnModLaunch a) {
 hipError_t launch_ln_modulate(const LnModLaunch &a, hipStream_t s) {
     const dim3 grid((a.L + kRowsPerBlock - 1) / kRowsPerBlock);
     const int cpl = (a.hidden / 8 + 63) / 64;
-    if (cpl <= 4) ln_modulate_kernel<4><<<grid, kThreads, 0, s>>>(a);
-    else if (cpl <= 8) ln_modulate_kernel<8><<<grid, kThreads, 0, s>>>(a);
-    else if (cpl <= 12) ln_modulate_kernel<12><<<grid, kThreads, 0, s>>>(a);
-    else ln_modulate_kernel<16><<<grid, kThreads, 0, s>>>(a);
+    if (a.stats && (a.stats_groups < 1 || a.stats_groups > 64 || a.stats_groups * a.stats_gw != a.hidden))
+        return hipErrorInvalidValue;
+    if (a.stats) {
+        if (cpl <= 4) ln_modulate_kernel<4, true><<<grid, kThreads, 0, s>>>(a);
+        else if (cpl <= 8) ln_modulate_kernel<8, true><<<grid, kThreads, 0, s>>>(a);
+        else if (cpl <= 12) ln_modulate_kernel<12, true><<<grid, kThreads, 0, s>>>(a);
+        else ln_modulate_kernel<16, true><<<grid, kThreads, 0, s>>>(a);
+    } else {
+        if (cpl <= 4) ln_modulate_kernel<4, false><<<grid, kThreads, 0, s>>>(a);
+        else if (cpl <= 8) ln_modulate_kernel<8, false><<<grid, kThreads, 0, s>>>(a);
+        else if (cpl <= 12) ln_modulate_kernel<12, false><<<grid, kThreads, 0, s>>>(a);
+        else ln_modulate_kernel<16, false><<<grid, kThreads, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 

@@ -192,3 +192,29 @@ def test_token_reduction_host_side_argument_errors(lib):
     assert lib.pma_token_plan_check(100, 50, fake, fake, None, None, None, None, None) == 1
     assert lib.pma_token_plan_check(100, 50, fake, fake, ctypes.c_void_p(258), None, None, None,
                                     None) == 3
+
+
+def test_gate_ln_host_side_argument_errors(lib):
+    n = ctypes.c_size_t()
+    fake = ctypes.c_void_p(256)
+    p = B.block_params(5376, 14336, 2688, 56)
+    # at most hidden / 128 = 42 (mean, M2) fp32 pairs per row
+    assert lib.pma_gate_ln_workspace_size(ctypes.byref(p), 8192, ctypes.byref(n)) == 0
+    assert n.value == 8192 * 42 * 8
+    assert lib.pma_gate_ln_workspace_size(ctypes.byref(p), 0, ctypes.byref(n)) == 2
+    assert lib.pma_gate_ln_workspace_size(ctypes.byref(p), 100, None) == 1
+    lay = B.Layout(8192, 1, 256, 64, 32, 128, fake, fake, fake, fake, fake, fake, fake, fake,
+                   fake, fake)
+    f = lib.pma_gate_residual_ln_modulate
+
+    def call(gate_chunk=2, which=1, b=fake, ws=fake, ws_bytes=1 << 40, K=7168):
+        return f(ctypes.byref(p), ctypes.byref(lay), fake, 7168, K, fake, fake, gate_chunk, fake,
+                 fake, fake, which, b, ws, ws_bytes, None)
+
+    assert call(which=2) == 2
+    assert call(gate_chunk=3) == 2
+    assert call(b=None) == 1
+    assert call(ws=None) == 1
+    assert call(ws=ctypes.c_void_p(128)) == 3
+    assert call(ws_bytes=8192 * 42 * 8 - 1) == 4
+    assert call(K=100) == 2          # K % 64 != 0, caught by the projection's checks

@@ -160,6 +160,66 @@ def test_linear_epilogues_match_numpy(epi, M, N, K):
     assert not bad.any(), f"{int(bad.sum())} values off; worst {err.max()}"
 
 
+@pytest.mark.parametrize("M,N,K,offset", [(1, 256, 64, 0.0), (257, 512, 448, 0.0),
+                                            (300, 1792, 192, 0.0), (300, 1792, 320, 100.0),
+                                            (1000, 5376, 256, 0.0)])
+def test_gate_residual_ln_modulate_fused(M, N, K, offset):
+    """The gated residual with the row statistics in its epilogue, then the
+    norm from those statistics: x1 bit-equal to pma_linear's GATE_RESIDUAL,
+    b within one bf16 rounding of the fp64 LN-modulate of that x1 (and of
+    the unfused pma_ln_modulate).  N = 1792 and 5376 run 224-wide tiles
+    (groups of 224 columns), 256 and 512 the 256-wide ones (groups of 128);
+    the residual offset of 100 makes the mean dominate the variance; the
+    gate and the modulation come from different tables and chunks (a
+    block's fc2 feeding the next block's first norm) in half the cases."""
+    import torch
+    from packed_masked_attention_amd import binding as B
+    rng = np.random.default_rng(20 + M + K)
+    T = 2
+    say(f"gate residual + ln modulate M={M} N={N} K={K} offset={offset}")
+    tags = rng.integers(0, 3, M).astype(np.int32)
+    tags[M - M // 10:] = -1
+    ts = rng.integers(0, T, M).astype(np.int32)
+    ts[tags == -1] = 0
+    lay = synth.layout_from_tags(tags, np.zeros((M, 3), np.int32), ts, T)
+    p = B.block_params(N, 512, 64, 2)
+    dl = B.pma_layout_build(lay)
+    A = synth.normal_bf16(rng, (M, K))
+    W = synth.normal_bf16(rng, (N, K), 0.05)
+    xr = synth.f32_to_bf16_bits(rng.standard_normal((M, N), dtype=np.float32) + np.float32(offset))
+    t1 = rng.standard_normal((3, T, 6, N)).astype(np.float32)
+    t2 = rng.standard_normal((3, T, 6, N)).astype(np.float32)
+    cross = K % 128 == 64   # fc2 -> the next block's first norm
+    gate_chunk, which = (5, 0) if cross else (2, 1)
+    dA, dW, dx = to_dev_bf16(A), to_dev_bf16(W), to_dev_bf16(xr)
+    dt1 = torch.from_numpy(t1).cuda()
+    dt2 = torch.from_numpy(t2).cuda() if cross else dt1
+    dtags, dts = torch.from_numpy(tags).cuda(), torch.from_numpy(ts).cuda()
+    nan = lambda: torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    x1, b, x1_ref, b_ref = nan(), nan(), nan(), nan()
+    B.pma_gate_residual_ln_modulate(p, dl, dA, K, K, dW, dt1, gate_chunk, dx, x1, dt2, which, b)
+    B.pma_linear(M, N, K, dA, K, dW, K, x1_ref, N, 1, R=dx, ldr=N, table=dt1, num_timesteps=T,
+                 gate_chunk=gate_chunk, tags=dtags, ts_idx=dts)
+    B.pma_ln_modulate(p, dl, dt2, which, x1_ref, b_ref)
+    torch.cuda.synchronize()
+    assert torch.equal(x1.view(torch.int16), x1_ref.view(torch.int16)), "x1 differs"
+    x1_64 = bf16_to_np(x1)
+    mod = (t2 if cross else t1).astype(np.float64)
+    ref = oblock.ln_modulate(x1_64, mod, tags, ts, "a" if which == 0 else "f", 1e-5)
+    got = bf16_to_np(b)
+    bound = np.abs(ref) * 2.0 ** -8 * 1.02 + 1e-5 * np.abs(ref).max()
+    bad = np.abs(got - ref) > bound
+    assert not bad.any(), f"{int(bad.sum())} values beyond one rounding of the oracle"
+    # the unfused norm meets the same bound; the two differ only where their
+    # fp32 statistics round differently (outputs near zero, where the
+    # bound's floor dominates, can then differ by a few ulps)
+    plain = bf16_to_np(b_ref)
+    assert not (np.abs(plain - ref) > bound).any(), "unfused norm beyond one rounding"
+    diff = got != plain
+    say(f"  b: {int(diff.sum())} of {diff.size} differ from the unfused norm")
+    assert diff.mean() < 0.01
+
+
 @pytest.mark.parametrize("epi", [0, 1])
 def test_linear_tile_shapes_agree(epi):
     """The O-projection shape (N = 5376, K = 7168) at M = 8192 runs 224-wide
