@@ -9,7 +9,9 @@
 //
 // A skinny GEMM (T distinct timesteps x 3*6*hidden outputs) bound by reading
 // the 3 x 6*hidden x E bf16 weights once: 16 lanes per weight row read it in
-// 16-byte chunks; the T embeddings sit in LDS; fp32 accumulation.
+// 16-byte chunks, four in flight per lane and nontemporal (read once: 89.9 ->
+// 79.6 us for 520 MB, 6.5 TB/s); the T embeddings sit in LDS; fp32
+// accumulation.
 #include "internal.h"
 
 namespace pma {
@@ -32,8 +34,9 @@ __global__ __launch_bounds__(kThreads) void adaln_table_kernel(AdaLnLaunch a) {
     float acc[kMaxT];
 #pragma unroll
     for (int t = 0; t < kMaxT; ++t) acc[t] = 0.f;
+#pragma unroll 4
     for (int e = gl * 8; e < a.E; e += 128) {
-        const u16x8 wr = *reinterpret_cast<const u16x8 *>(w + e);
+        const u16x8 wr = __builtin_nontemporal_load(reinterpret_cast<const u16x8 *>(w + e));
         float wf[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) wf[j] = bf16_bits_to_f32(wr[j]);
