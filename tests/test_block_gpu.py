@@ -493,9 +493,16 @@ def test_block_stages_full_size():
     B.pma_linear(L, hid, ffn, h, ffn, r.w_fc2, ffn, x2, hid, 1, R=x1, ldr=hid, table=r.table,
                  num_timesteps=1, gate_chunk=5, tags=r.dl.arrays["tags"],
                  ts_idx=r.dl.arrays["ts_idx"])
+    # a7 + a8 through the fused entry point (row statistics in the projection's
+    # epilogue) on the same O: x1 bit for bit, b against the oracle below
+    x1f, bf = dev((L, hid)), dev((L, hid))
+    B.pma_gate_residual_ln_modulate(r.p, r.dl, o, HD, HD, r.w_o, r.table, 2, r.x, x1f, r.table, 1,
+                                    bf)
     torch.cuda.synchronize()
+    assert torch.equal(x1f.view(torch.int16), x1.view(torch.int16)), "fused x1 differs"
     x = oracle.bf16_to_f64(inp["x"])
     a_g, qkv_g, o_g, x1_g, b_g, h_g, x2_g = (f64(t) for t in (a, qkv, o, x1, b, h, x2))
+    bf_g = f64(bf)
     stage("a", a_g[rows], oblock.ln_modulate(x[rows], mod, tags[rows], ts[rows], "a", 1e-5))
     wq = oracle.bf16_to_f64(inp["w_qkv"])
     stage("qkv", qkv_g[rows], a_g[rows] @ wq.T)
@@ -507,7 +514,9 @@ def test_block_stages_full_size():
     stage("o", o_g[rows], o_ref.reshape(rows.size, HD), floor=1e-2)
     gate_a = oblock.row_modulation(mod, tags, ts, oblock.GATE_A)[rows]
     stage("x1", x1_g[rows], x[rows] + gate_a * (o_g[rows] @ oracle.bf16_to_f64(inp["w_o"]).T))
-    stage("b", b_g[rows], oblock.ln_modulate(x1_g[rows], mod, tags[rows], ts[rows], "f", 1e-5))
+    b_ref = oblock.ln_modulate(x1_g[rows], mod, tags[rows], ts[rows], "f", 1e-5)
+    stage("b", b_g[rows], b_ref)
+    stage("b (fused gate + norm)", bf_g[rows], b_ref)
     w1 = oracle.bf16_to_f64(inp["w_fc1"])
     g_ = b_g[rows] @ w1[:ffn].T
     u_ = b_g[rows] @ w1[ffn:].T
