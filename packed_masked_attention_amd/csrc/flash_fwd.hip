@@ -284,6 +284,19 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
             }
             continue;
         }
+        // ---- Q^T fragments: lane holds query row l32, channels 16c + 8*hi + [0, 8)
+        // (requested before the tile list is copied, so the two loads' latencies
+        // overlap)
+        const int q0 = qt * kBM + wave * 32;
+        bf16x8 qf[8];
+        {
+            const uint16_t *qrow = a.qh + ((int64_t)head * a.Lp + q0 + l32) * kD + 8 * hi;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * c);
+        }
+        const int qrow = q0 + l32;
+        const int dq = (uint32_t)qrow < (uint32_t)a.L ? a.doc[qrow] : 0;
+
         {
             const int32_t *list = a.list + (int64_t)qt * a.nkt + beg;
             const uint8_t *cls = a.cls + (int64_t)qt * a.nkt;
@@ -302,17 +315,6 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
             make_rsrc(a.vt + (int64_t)head * kD * a.Lp, (uint32_t)a.Lp * kD * 2u);
         // keys past the sequence read as document 0 here; the mask adds the bound
         const __amdgpu_buffer_rsrc_t drs = make_rsrc(a.doc, (uint32_t)a.L * 4u);
-
-        // ---- Q^T fragments: lane holds query row l32, channels 16c + 8*hi + [0, 8)
-        const int q0 = qt * kBM + wave * 32;
-        bf16x8 qf[8];
-        {
-            const uint16_t *qrow = a.qh + ((int64_t)head * a.Lp + q0 + l32) * kD + 8 * hi;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * c);
-        }
-        const int qrow = q0 + l32;
-        const int dq = (uint32_t)qrow < (uint32_t)a.L ? a.doc[qrow] : 0;
 
         // ---- LDS-DMA lane offsets.  Wave-instruction j of the K tile fills rows
         // 4j..4j+3 (lane l: row 4j + l/16, position l%16); of the V^T tile, rows
