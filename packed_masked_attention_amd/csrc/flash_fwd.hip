@@ -42,12 +42,13 @@
 //  * K, V^T tiles (64 keys) stream through a 4-deep LDS ring filled by
 //    direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds) with the tile
 //    offset in an SGPR.  Every wave issues its share of tile t+3's K and
-//    t+2's V^T during its G(t), one instruction every few MFMAs (issued in
-//    a burst at the phase start, the instructions of the four waves queue
-//    behind each other and hold back the first MFMAs); phase ends wait for
-//    all but the newest one or two batches, so each batch has about three
-//    phases to land and no wave waits for a tile it just requested.  The 64 document ids of a V
-//    tile's keys ride along in the same slot (for the rare masked tile).
+//    t+2's V^T at the start of its softmax phase S(t), so the MFMA phase's
+//    issue slots stay with the MFMAs and their fragment reads (issued inside
+//    the MFMA phase, even spread one every few MFMAs, they cost 2-8%); every
+//    phase end waits for all but the newest batch, so a batch lands within
+//    S(t), G(t+1) and S(t+1) and no wave waits for a tile it just requested.
+//    The 64 document ids of a V tile's keys ride along in the same slot (for
+//    the rare masked tile).
 //    Each 1 KB wave-instruction fills LDS in lane order, so instead of row
 //    padding the 16-byte chunks of a row are XOR-swizzled (chosen by the
 //    global address each lane fetches), which keeps the MFMA-operand reads
@@ -374,18 +375,9 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
         bf16x8 vpre[kVPre];
 
         // ---- MFMA phase: O^T += V(t-1)^T P(t-1)^T (when withpv), S(t) = K(t) Q^T - mu
-        auto gphase = [&](bool withpv, const uint16_t *vr, const uint16_t *kr, int dk, uint16_t *dks,
-                          int dv, uint16_t *dvs) __attribute__((always_inline)) {
-            // the document-id DMA (8 lanes) ahead of the scheduled region: its
-            // lane branch would split the MFMA block
-            dma_id(dv, dvs);
+        auto gphase = [&](bool withpv, const uint16_t *vr, const uint16_t *kr)
+                          __attribute__((always_inline)) {
             __builtin_amdgcn_s_setprio(1);
-            if (!withpv) {
-                // the first tile has no PV half to spread them over
-                dma_k(dk, dks);
-#pragma unroll
-                for (int i = 0; i < kKI; ++i) dma_v1(dv, dvs, i);
-            }
             if (withpv) {
                 // channel blocks interleaved so consecutive MFMAs are independent
 #pragma unroll
@@ -399,11 +391,6 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
                                       : *reinterpret_cast<const bf16x8 *>(
                                             vr + d * kBN + 8 * v_pos(d, 2 * cc + hi));
                         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[cc], o[db], 0, 0, 0);
-                        // this wave's share of the ring refill, spread over the
-                        // phase rather than issued in one burst (kKI == 2)
-                        if (f == 2) dma_k1(dk, dks, 0);
-                        if (f == 8) dma_k1(dk, dks, 1);
-                        if (f == 14) dma_v1(dv, dvs, 0);
                     }
             }
 #pragma unroll
@@ -416,24 +403,29 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
                     // the first k-step starts from the seed -mu
                     s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], c == 0 ? sd : s[kb],
                                                                     0, 0, 0);
-                    if (withpv && c == 2 && kb == 1) dma_v1(dv, dvs, 1);
                 }
-            // LDS fragment reads run kReadAhead ahead of their MFMAs; the DMA
-            // instructions sit between MFMAs
+            // LDS fragment reads run kReadAhead ahead of their MFMAs
             __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);
 #pragma unroll
             for (int i = 0; i < 32; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                if (i == 2 || i == 8 || i == 14 || i == 21)
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
             __builtin_amdgcn_s_setprio(0);
         };
 
-        // ---- softmax phase of tile t (list entry e, V(t) slot vn): mask,
+        // ---- softmax phase of tile t (list entry e, V(t) slot vn): this wave's
+        // share of DMA(t) = {K(t+3) into slot dks, V(t+2) into dvs}, mask,
         // lazy-max softmax -> P(t)^T in bf16, O rescale
-        auto sphase = [&](int e, const uint16_t *vn) __attribute__((always_inline)) {
+        auto sphase = [&](int e, const uint16_t *vn, int dk, uint16_t *dks, int dv, uint16_t *dvs)
+                          __attribute__((always_inline)) {
+            // the ring refill first: the earlier it goes out, the longer it
+            // has to land (issued after the V pre-reads or at the end of the
+            // phase, 0.4% and 0.9% slower)
+            dma_id(dv, dvs);
+            dma_k(dk, dks);
+#pragma unroll
+            for (int i = 0; i < kKI; ++i) dma_v1(dv, dvs, i);
             // V(t) fragments for the first MFMAs of the next PV, read while the
             // softmax runs
 #pragma unroll
@@ -538,10 +530,11 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
         // Global phase p: group 0 runs G(t) at p = 2t and S(t) at 2t + 1; group 1
         // runs one phase later.  Tile x sits in ring slot x % 4.  K(t) is read in
         // phases 2t, 2t+1; V(t) in 2t+1 .. 2t+3.  Each wave issues its share of
-        // DMA(t) = {K(t+3), V(t+2)} during its G(t) (the slots of K(t-1) and
-        // V(t-2), both done with by the end of phase 2t-1); the waits at
-        // phase ends (two batches may stay in flight after G, one after S) make
-        // DMA(t) land by the end of phase 2t+4, before either tile is first read.
+        // DMA(t) = {K(t+3), V(t+2)} at the start of its S(t) (phase 2t+1 or
+        // 2t+2: the slots of K(t-1) and V(t-2), both done with by the end of
+        // phase 2t-1).  Every phase end leaves only the newest batch in flight,
+        // so DMA(t) has landed by the end of S(t+1) (phase 2t+3 or 2t+4),
+        // before V(t+2) is first read (phase 2t+5) or K(t+3) (2t+6).
         if (grp == 1) PMA_PHASE_END(0);
 
         // list entries of the current tile t: ce = entry t, ck = entry t+3 (the
@@ -556,10 +549,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
         auto tile = [&](int t, bool withpv, uint16_t *k_r, uint16_t *k_m, uint16_t *v_r,
                         uint16_t *v_p, uint16_t *v_q) __attribute__((always_inline)) {
             const int e = ce;
-            gphase(withpv, v_p, k_r, ck & kMask, k_m, cv & kMask, v_q);
-            PMA_PHASE_END(2 * kNDMA);
+            gphase(withpv, v_p, k_r);
+            PMA_PHASE_END(kNDMA);
             const int ne = tlist[t + 1], nk = tlist[t + 4], nv = tlist[t + 3];
-            sphase(e, v_r);
+            sphase(e, v_r, ck & kMask, k_m, cv & kMask, v_q);
             ce = __builtin_amdgcn_readfirstlane(ne);
             ck = __builtin_amdgcn_readfirstlane(nk);
             cv = __builtin_amdgcn_readfirstlane(nv);
