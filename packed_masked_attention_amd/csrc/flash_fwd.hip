@@ -103,7 +103,6 @@ static_assert(kFlashQueueBytes >= 16 * sizeof(int32_t), "the queue reset clears 
 constexpr int kStaticLds = 4 * kTileElems * 2 + 4 * (((kTileElems + 2 * kBN) * 2 + 1023) / 1024 * 1024) + 1024;
 constexpr int kLdsBytes = 160 * 1024;      // per workgroup on gfx950
 static_assert(kKI * kNW == 16, "16 KB tiles split over the waves");
-static_assert(kKI == 2, "the MFMA phase spreads two K and two V^T DMA instructions per wave");
 
 // LDS placement of 16-byte chunk c of a tile row:
 //   K tile   [64 keys][16 chunks]: position c ^ (row & 15)
