@@ -199,7 +199,7 @@ pma_status pma_qk_norm_rope(const pma_attn_params *p, const pma_layout *layout,
 
 /* Bytes of the optional workspace of pma_flash_attention: 256 bytes of
  * work-queue counters, then the partial results of the items whose key
- * ranges are split (none below 12288 keys), then (when any item is split)
+ * ranges are split (none below 8192 keys), then (when any item is split)
  * 32 KiB of clock stamps: for each persistent workgroup of the last call
  * (at most 1024, one per CU), four u64 -- the shader clock counter and the
  * 100 MHz real-time counter at its start, the same two at its end -- from
@@ -217,11 +217,11 @@ pma_status pma_flash_workspace_size(const pma_attn_params *p, int32_t seq_len, s
  *   lse: fp32 [H][L] natural-log sum of exp of the scaled logits (NULL: not written).
  *   workspace: NULL, or >= pma_flash_workspace_size() bytes, 256-byte aligned,
  *        owned by the caller and overwritten (contents need no clearing).
- *        From 12288 keys on, it holds a work queue: one workgroup per CU
+ *        From 8192 keys on, it holds a work queue: one workgroup per CU
  *        pulls (head, q-tile) items, first its own XCD's then what is left of
- *        the others', and the last items of every XCD's share run as four
- *        parts over their key ranges, whose partial softmax results a second
- *        kernel merges.  Shorter sequences, or NULL, run one item per
+ *        the others', and the last items of every XCD's share run as two
+ *        (below 12288 keys) or four parts over their key ranges, whose
+ *        partial softmax results a second kernel merges.  Shorter sequences, or NULL, run one item per
  *        workgroup.  The two agree to fp32 rounding order (each part rounds
  *        its probabilities to bf16 against its own running maximum).
  *        Calls that share one workspace must not overlap.
@@ -240,7 +240,7 @@ pma_status pma_flash_attention(const pma_attn_params *p, const pma_layout *layou
  * array of PMA_FLASH_STATIC_SCRATCH_BYTES (32 MiB) that every GPU the library
  * runs on holds until the process ends.  The array bounds the key-range
  * split to the items it holds: up to 7 split items per XCD (the workspace
- * form takes up to 16), so from 12288 keys on the two forms agree to fp32
+ * form takes up to 16), so from 8192 keys on the two forms agree to fp32
  * rounding order, and below that bit for bit.  No shape is refused for the
  * array's size.  The call allocates nothing; the counters are cleared by a
  * kernel on the stream at every call.  All calls on one GPU share its array:

@@ -70,7 +70,8 @@
 //    padding q-tiles) and XCDs of unequal speed (on MI355X up to 10% apart
 //    on the same items) leave others idle.  The last units are parts: the
 //    last kSplitItems items of every XCD's share, each split over
-//    consecutive quarters of its key list, so the final units are short.  A
+//    consecutive halves (below 12288 keys) or quarters of its key list, so
+//    the final units are short.  A
 //    part writes its unnormalised O, reference max and row sum, and
 //    flash_merge_kernel combines the parts (the split form of the online
 //    softmax: weights 2^(m_p - m) on each part's O and row sum).
@@ -92,8 +93,9 @@ constexpr int kReadAhead = 3;              // LDS fragment reads in flight ahead
 constexpr int kVPre = 2;                   // V fragments read during the softmax phase
 constexpr int kMask = 0x3fffffff;          // list entry -> k-tile index
 constexpr int kSplitItems = 16;            // items per XCD split over their key range
-constexpr int kSplitMinKeyTiles = 192;     // no split below this many k-tiles (12288 keys)
-constexpr int kSplitParts = 4;             // workgroups per split item
+constexpr int kSplitMinKeyTiles = 128;     // no work queue below this many k-tiles (8192 keys)
+constexpr int kMaxSplitParts = 4;          // partial-result slots per split item
+constexpr int kFourPartMinKeyTiles = 192;  // 4 parts per split item from here (12288 keys), 2 below
 // one part's partial result: O [kBM rows][kD] fp32, then (m, l) per row
 constexpr int kPartFloats = kBM * kD + 2 * kBM;
 static_assert(kFlashQueueBytes >= 16 * sizeof(int32_t), "the queue reset clears 16 counters");
@@ -174,10 +176,17 @@ __device__ __forceinline__ float half_sum(float x) {
 // one, the workgroups persist (one per CU) and pull units until none is left:
 // first the items of their own XCD's share (local indices [0, per_xcd - S),
 // in order, so its heads' K/V stay in its L2), then the remaining items of
-// the other XCDs' shares (neighbours first), then the kSplitParts parts of
+// the other XCDs' shares (neighbours first), then the split_parts parts of
 // the last S items of every share: its own XCD's parts first (their heads'
 // K/V sit in its L2), then the others' (neighbours first).  An XCD that runs
 // ahead takes over the tail of a slower one's share.
+// Workgroups per split item: 2 below 12288 keys, 4 from there (at 8192 keys,
+// 1.4513 ms with 2 parts, 1.4724 with 4, 1.4743 without the queue; at 16384
+// keys 2 or 8 parts were 0.5-0.7% slower than 4).
+__device__ __forceinline__ int split_parts(const FlashLaunch &a) {
+    return a.nkt < kFourPartMinKeyTiles ? 2 : kMaxSplitParts;
+}
+
 __device__ __forceinline__ int2 next_work(const FlashLaunch &a, int xcd, int iter) {
     const int total = a.H * a.nqt;
     const int per_xcd = (total + 7) / 8;
@@ -185,7 +194,7 @@ __device__ __forceinline__ int2 next_work(const FlashLaunch &a, int xcd, int ite
         const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
         return make_int2(iter == 0 && item < total ? item : -1, -1);
     }
-    const int S = a.split_items;
+    const int S = a.split_items, P = split_parts(a);
     for (int k = 0; k < 8; ++k) {
         const int y = (xcd + k) & 7;
         const int own = min(per_xcd - S, max(0, total - y * per_xcd));
@@ -199,13 +208,13 @@ __device__ __forceinline__ int2 next_work(const FlashLaunch &a, int xcd, int ite
     // other XCDs' (neighbours first)
     for (int k = 0; k < 8; ++k) {
         const int y = (xcd + k) & 7;
-        if (__hip_atomic_load(&a.queue[8 + y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= S * kSplitParts)
+        if (__hip_atomic_load(&a.queue[8 + y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= S * P)
             continue;
         for (;;) {
             const int g = atomicAdd(&a.queue[8 + y], 1);
-            if (g >= S * kSplitParts) break;
-            const int item = y * per_xcd + per_xcd - S + g / kSplitParts;
-            if (item < total) return make_int2(item, g % kSplitParts);
+            if (g >= S * P) break;
+            const int item = y * per_xcd + per_xcd - S + g / P;
+            if (item < total) return make_int2(item, g % P);
         }
     }
     return make_int2(-1, -1);
@@ -269,12 +278,13 @@ __global__ __launch_bounds__(kNW * 64, 1) void flash_fwd_kernel(FlashLaunch arg)
         const int head = item / a.nqt;
         const int qt = a.order[item % a.nqt];
         const int full = a.count[qt];
-        const int beg = part < 0 ? 0 : part * full / kSplitParts;
-        const int cnt = part < 0 ? full : (part + 1) * full / kSplitParts - beg;
+        const int nparts = split_parts(a);
+        const int beg = part < 0 ? 0 : part * full / nparts;
+        const int cnt = part < 0 ? full : (part + 1) * full / nparts - beg;
         // a part's partial result: slot of (owning XCD, split item, part)
         const int owner = item / per_xcd, sidx = item % per_xcd - (per_xcd - a.split_items);
         float *pres = part < 0 ? nullptr
-                               : a.part + (int64_t)((owner * a.split_items + sidx) * kSplitParts + part) *
+                               : a.part + (int64_t)((owner * a.split_items + sidx) * kMaxSplitParts + part) *
                                               kPartFloats;
         if (cnt == 0) {
             // an empty key range: a part with no weight
@@ -662,18 +672,23 @@ __global__ __launch_bounds__(256) void flash_merge_kernel(FlashLaunch a) {
     const int r = rb * 8 + (int)(threadIdx.x >> 5), c4 = (int)(threadIdx.x & 31);
     const int qrow = qt * kBM + r;
     if (qrow >= a.L) return;
-    const float *base = a.part + (int64_t)gi * kSplitParts * kPartFloats;
-    float mp[kSplitParts], lp[kSplitParts], m = -INFINITY;
+    const float *base = a.part + (int64_t)gi * kMaxSplitParts * kPartFloats;
+    const int nparts = split_parts(a);
+    float mp[kMaxSplitParts], lp[kMaxSplitParts], m = -INFINITY;
 #pragma unroll
-    for (int p = 0; p < kSplitParts; ++p) {
-        mp[p] = base[p * kPartFloats + kBM * kD + 2 * r];
-        lp[p] = base[p * kPartFloats + kBM * kD + 2 * r + 1];
+    for (int p = 0; p < kMaxSplitParts; ++p) {
+        mp[p] = -INFINITY;
+        lp[p] = 0.f;
+        if (p < nparts) {
+            mp[p] = base[p * kPartFloats + kBM * kD + 2 * r];
+            lp[p] = base[p * kPartFloats + kBM * kD + 2 * r + 1];
+        }
         if (lp[p] > 0.f) m = fmaxf(m, mp[p]);
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float l = 0.f;
 #pragma unroll
-    for (int p = 0; p < kSplitParts; ++p) {
+    for (int p = 0; p < kMaxSplitParts; ++p) {
         if (!(lp[p] > 0.f)) continue;
         const float w = __builtin_amdgcn_exp2f(mp[p] - m);
         l = fmaf(w, lp[p], l);
@@ -693,8 +708,9 @@ __global__ __launch_bounds__(256) void flash_merge_kernel(FlashLaunch a) {
 
 int32_t flash_split_items(int32_t H, int32_t L) {
     // below kSplitMinKeyTiles an item is short enough that the queue's fetch
-    // and the parts' set-up cost more than the balance gains (measured: 4%
-    // slower at 4096 keys, 2-4% faster from 16384); 0 turns the queue off
+    // and the parts' set-up cost more than the balance gains (measured: 1-10%
+    // slower at 4096 keys, 1.6% faster at 8192 with 2 parts per split item,
+    // 2-4% faster from 16384 with 4); 0 turns the queue off
     const int nqt = (L + kBM - 1) / kBM, nkt = (L + kBN - 1) / kBN;
     if (nkt < kSplitMinKeyTiles) return 0;
     const int per_xcd = (H * nqt + 7) / 8;
@@ -702,7 +718,7 @@ int32_t flash_split_items(int32_t H, int32_t L) {
 }
 
 size_t flash_split_bytes_for(int32_t split_items) {
-    return kFlashQueueBytes + (size_t)8 * split_items * kSplitParts * kPartFloats * sizeof(float);
+    return kFlashQueueBytes + (size_t)8 * split_items * kMaxSplitParts * kPartFloats * sizeof(float);
 }
 
 size_t flash_split_bytes(int32_t H, int32_t L) { return flash_split_bytes_for(flash_split_items(H, L)); }

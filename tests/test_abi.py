@@ -69,9 +69,15 @@ def test_host_side_argument_errors(lib):
     # then 1024 workgroups x 4 clock stamps of 8 bytes
     stamps = 1024 * 4 * 8
     assert fw.value == 256 + 8 * 16 * 4 * 256 * 130 * 4 + stamps
-    # below 192 k-tiles (12288 keys) nothing is split: the counters alone
+    # below 128 k-tiles (8192 keys) nothing is split: the counters alone
     assert lib.pma_flash_workspace_size(ctypes.byref(B.attn_params(2)), 100, ctypes.byref(n)) == 0
     assert n.value == 256
+    assert lib.pma_flash_workspace_size(ctypes.byref(B.attn_params(2)), 8128, ctypes.byref(n)) == 0
+    assert n.value == 256
+    # from 128 k-tiles on: 2 heads x 32 q-tiles, 8 items per XCD, all split;
+    # four part slots per item (two used below 12288 keys)
+    assert lib.pma_flash_workspace_size(ctypes.byref(B.attn_params(2)), 8192, ctypes.byref(n)) == 0
+    assert n.value == 256 + 8 * 8 * 4 * 256 * 130 * 4 + stamps
     assert lib.pma_flash_workspace_size(ctypes.byref(B.attn_params(2)), 12288, ctypes.byref(n)) == 0
     # 2 heads x 48 q-tiles: 12 items per XCD, all 12 split
     assert n.value == 256 + 8 * 12 * 4 * 256 * 130 * 4 + stamps

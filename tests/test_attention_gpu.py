@@ -292,13 +292,15 @@ def test_attention_call_options():
 @pytest.mark.parametrize("case", [
     ("L12300_tail_pad", (61, 12300, 2, 12 / 12300, False)),
     ("L13000_scattered", (62, 13000, 3, 0.15, True)),
+    ("L9000_two_parts", (63, 9000, 2, 0.1, True)),
 ])
 def test_attention_key_range_split(case):
     """The work queue with the key-range split (flash workspace given) against
     one item per workgroup (no workspace) and the oracle on sampled rows.
-    Past 12288 keys the last items of each XCD's share run in 4 parts; with 2
-    or 3 heads every item is among them.  At L=12300 the last q-tile holds
-    only the 12 padding rows, whose one k-tile leaves three parts empty."""
+    From 8192 keys the last items of each XCD's share run in 2 parts, from
+    12288 keys in 4; with 2 or 3 heads every item is among them.  At L=12300
+    the last q-tile holds only the 12 padding rows, whose one k-tile leaves
+    three parts empty."""
     import torch
     name, args = case
     inp = _random_inputs(*args)

@@ -5,7 +5,7 @@ the C ABI.  The calls run in a row, larger inputs first, so later calls find
 the array holding an earlier call's contents.
 
 Where both forms split the same items (fewer than 8 split items per XCD, or
-no split below 12288 keys) they must agree bit for bit; where the array
+no split below 8192 keys) they must agree bit for bit; where the array
 bounds the split to 7 items per XCD they agree to the rounding of the split
 (each part rounds its probabilities against its own running maximum): per
 element within 2^-7 of the |v| ~ 1 scale plus the output rounding, 2.5e-4 on
@@ -42,6 +42,7 @@ _CASES = [
     ("L13000_H4_split_bounded", 101, 13000, 4, 0.12, False, False),   # 16 vs 7 split items per XCD
     ("L12400_H1_same_split", 102, 12400, 1, 0.1, True, True),         # 7 items per XCD either way
     ("L700_H2_no_split", 103, 700, 2, 0.15, True, True),              # one item per workgroup
+    ("L9000_H1_two_parts", 105, 9000, 1, 0.1, True, True),            # 5 items per XCD, 2 parts
 ]
 
 
