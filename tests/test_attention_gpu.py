@@ -464,3 +464,36 @@ def test_attention_global_position_shift(delta):
     _gpu_pair_close(b.out(), a.out(), "shifted vs unshifted")
     # the Q' of a shifted row does change: the test is not vacuous
     assert not np.array_equal(bf16_to_np(a.qh), bf16_to_np(b.qh))
+
+
+@pytest.mark.parametrize("pad", [1016, 1004])
+def test_attention_maximum_length(pad):
+    """The longest sequence the kernel's LDS tile list holds: 6908 k-tiles of
+    64 keys (442,112 rows; with pad=1004 the last k-tile is ragged, 52 rows).
+    The pages' packed structure at that length: 4096 text rows, a (27, 80, 200)
+    video grid, 5000 audio rows and the padding document at the tail; one head
+    keeps the run short.  Sampled rows against the fp64 oracle: rows of the
+    padding document, the first and last k-tile, the document boundaries and
+    random rows."""
+    H = 1
+    lay = synth.layout_from_counts(4096, (27, 80, 200), 5000, pad)
+    L = lay["L"]
+    assert -(-L // 64) == 6908
+    rng = np.random.default_rng(95 + pad)
+    q, k, v = (synth.normal_bf16(rng, (L, H, 128)) for _ in range(3))
+    inp = {"q": q, "k": k, "v": v, "layout": lay, "H": H, "D": 128}
+    tags = lay["tags"]
+    first_pad = int(np.flatnonzero(tags == -1)[0])
+    rows = {0, 1, 63, 64, 4095, 4096, first_pad - 1, first_pad, L - 64, L - 2, L - 1}
+    rows.update(range(L - 70, L - 60))
+    rows.update(rng.integers(first_pad, L, 12).tolist())
+    rows.update(rng.integers(0, first_pad, 40).tolist())
+    rows = np.array(sorted(rows), dtype=np.int32)
+    say(f"attention at the maximum length L={L}: {rows.size} sampled rows")
+    r = AttentionRun(inp).run()
+    got = r.out()
+    assert np.all(np.isfinite(got)), "every row written"
+    ref, lse = _oracle_o(inp, rows=rows)
+    st = assert_close(got[rows], ref, f"L={L}")
+    assert np.allclose(r.lse_np()[rows], lse, atol=2e-2, rtol=0), "lse"
+    say(f"  L={L} sampled rows ok: {st}")
